@@ -1,0 +1,202 @@
+"""Benchmark: one rank's causal bf16 ring of attention on one MI355X.
+
+A "step" is one whole emulated ring of the rank: state init, the P ring steps
+(side-stream staging of the next key/value block, double-buffered swaps, one
+ra_step launch per non-skipped block) and the finalize.  Inputs are seeded
+synthetic blocks already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank I]
+                    [--no-cpu-baseline]
+
+Prints ONE JSON line.  FLOPs count 4*head_dim per unmasked (query, key) pair
+per head (the diagonal block counts c(c+1)/2 pairs, skipped blocks none).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from ring_attention_block_amd import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "causal_bf16_h32_d128_c4096_p8"
+DEFAULT_RANK = 7
+
+
+def unmasked_pairs(wl, rank, rows=None):
+    """Unmasked (query, key) pairs of one head for `rank` (optionally only `rows`)."""
+    c = wl.rows
+    rows = np.arange(c) if rows is None else np.asarray(rows)
+    if not wl.causal:
+        return int(len(rows) * c * wl.blocks)
+    return int(np.sum(rank * c + rows + 1))
+
+
+def ring_flops(wl, rank):
+    return 4 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank)
+
+
+def full_step_flops(wl):
+    return 4 * wl.head_dim * wl.heads * wl.rows * wl.rows
+
+
+def generate(wl, rank, threads=16):
+    """Seeded blocks of the workload (Q of the rank, every K and V), in parallel;
+    each block has its own seed, so threading does not change any value."""
+    import concurrent.futures as cf
+    jobs = [(synth.ROLE_Q, rank)] + [(r, j) for j in range(wl.blocks)
+                                     for r in (synth.ROLE_K, synth.ROLE_V)]
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        arrs = list(ex.map(lambda rj: synth.block(wl, *rj), jobs))
+    return dict(zip(jobs, arrs))
+
+
+def cpu_baseline(wl, rank, blocks, target_s=15.0):
+    """The CPU fp64 oracle, as it stands, on a bounded sample of query rows."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _helpers import oracle_rank          # test plumbing around oracle/
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas")
+    except Exception:
+        blas_threads = None
+    cache = dict(blocks)
+    kv_blocks = list(range(rank + 1)) if wl.causal else list(range(wl.blocks))
+    n = 4
+    while True:
+        rows = synth.sample_rows(wl.seed, wl.rows, n)
+        t0 = time.perf_counter()
+        oracle_rank(wl, rank, kv_blocks, wl.causal, row_sel=rows, cache=cache)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n >= wl.rows:
+            break
+        n = min(wl.rows, int(n * max(2.0, target_s / 3 / max(dt, 1e-3))))
+    flops = 4 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank, rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} seeded query rows x {wl.heads} heads of rank {rank} "
+                      f"({flops / 1e9:.1f} GFLOP fp64, {dt:.1f} s; numpy BLAS threads for the "
+                      f"products, one thread for exp)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ring of one rank is emulated on a "
+              "single MI355X; runs on more than one GPU are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ring_attention_block_amd import _lib
+    from ring_attention_block_amd.ring import RingEmulator
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.lib()   # fails loudly if libra.so is missing
+
+    wl = synth.WORKLOADS[args.workload]
+    rank = args.rank if args.rank is not None else (
+        DEFAULT_RANK if wl.name == DEFAULT_WORKLOAD else wl.ranks[-1])
+    dev = "cuda"
+
+    blocks = generate(wl, rank)
+
+    def to_dev(x):
+        if wl.dtype == "bf16":
+            t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(x)
+        return t.reshape(1, *x.shape).to(dev)
+
+    q = to_dev(blocks[(synth.ROLE_Q, rank)])
+    kv = {j: (to_dev(blocks[(synth.ROLE_K, j)]), to_dev(blocks[(synth.ROLE_V, j)]))
+          for j in range(wl.blocks)}
+    st = _lib.State(1, wl.heads, wl.rows, wl.head_dim, device=dev)
+    compute = torch.cuda.Stream()
+    emu = RingEmulator(q.shape, q.dtype, dev, compute_stream=compute)
+    o_out = torch.empty(st.o.shape, dtype=torch.float32, device=dev)
+    lse_out = torch.empty(st.m.shape, dtype=torch.float32, device=dev)
+
+    def one_ring(timers=None):
+        emu.run(st, q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
+                step_timers=timers)
+        _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
+
+    for _ in range(args.warmup):
+        one_ring()
+    torch.cuda.synchronize()
+
+    timers = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_ring(timers)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms = elapsed / args.steps * 1e3
+    flops = ring_flops(wl, rank)
+    tflops = flops / (ms / 1e3) / 1e12
+
+    full = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_FULL]
+    diag = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_DIAG]
+    if full:
+        dom_ms, dom_flops, dom = float(np.mean(full)), full_step_flops(wl), "ra_step full"
+    else:
+        dom_ms = float(np.mean(diag))
+        dom_flops = 4 * wl.head_dim * wl.heads * (wl.rows * (wl.rows + 1) // 2)
+        dom = "ra_step diagonal"
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+
+    line = {
+        "metric": "causal bf16 ring-step attention TFLOP/s + % of MFMA peak (c=4096, d=128)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
+        "config": {"workload": wl.name, "rank": rank, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "rows_per_block": wl.rows, "blocks": wl.blocks,
+                   "causal": wl.causal, "tokens": wl.tokens, "flop_per_step": flops,
+                   "pct_of_mfma_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "kernel": dom,
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(dom_ms, 5),
+                     "launches": len(full) if full else len(diag),
+                     "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, rank, blocks)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+/*
+ * ra.h -- C ABI of one rank's ring step of softmax attention on gfx950.
+ *
+ * The operation (pages cited by title and section):
+ *   "Ring Attention Paper Breakdown: Blockwise Distributed Transformers for
+ *   Near-Infinite Context", section 2 (ring schedule): at ring step s rank i
+ *   holds key/value block j = (i - s) mod P and folds it into the running
+ *   softmax state of its resident query block Q_i; section 3 gives the update
+ *   of that state (row max m, normaliser l, unnormalised output O) and the
+ *   single division O / l after the last step.
+ *   "Ring Attention Math Deep", section "The online-softmax identity that makes
+ *   streaming legal": the same recurrence per query row.
+ *   "Ring Attention：把超长序列沿设备环流动", section "Causal Attention
+ *   让环不再完全对称": under a causal mask a block strictly in the future is
+ *   skipped, the diagonal block is masked element by element, earlier blocks
+ *   are used whole.
+ *
+ * Conventions common to every call
+ *   - Every pointer to tensor data is a device pointer (hipMalloc'd or torch
+ *     CUDA memory) owned by the caller.  The library never allocates, frees or
+ *     retains memory and never writes q, k or v.
+ *   - Tensors are dense row-major: q, k, v and o are [batch, heads, rows,
+ *     head_dim]; m, l and lse are [batch, heads, rows].  Every non-empty tensor
+ *     pointer must be 16-byte aligned.
+ *   - Every call is asynchronous and ordered on `stream` (0 = the null
+ *     stream); no call synchronises.  Buffers must stay valid and unmodified
+ *     until the stream has passed the call.
+ *   - All checks run on the host before anything is enqueued.  On a negative
+ *     return nothing was enqueued and the state is untouched; ra_last_error()
+ *     then names the check that failed.  RA_ERR_HIP means a HIP launch or copy
+ *     failed to enqueue.  No exception or abort crosses this boundary.
+ *   - Calls that share a state or an output must not overlap on different
+ *     streams unless the caller orders them with events.
+ */
+#ifndef RA_H_
+#define RA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = -1,  /* bad shape, index, pointer, alignment or scale   */
+  RA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, kv_rows)   */
+  RA_ERR_HIP = -3           /* HIP refused to enqueue a kernel or copy         */
+} ra_status;
+
+typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* Result of the causal case test (ra_step_case). */
+typedef enum { RA_CASE_SKIP = 0, RA_CASE_DIAG = 1, RA_CASE_FULL = 2 } ra_case;
+
+/*
+ * Running online-softmax state of one rank's query block ("Ring Attention
+ * Paper Breakdown ...", section 3: m, l in R^c and O in R^{c x d} per head,
+ * kept on the rank for the whole ring).  All buffers are caller-owned fp32
+ * device memory.
+ *   m  [batch, heads, rows]           running maximum of the scaled scores
+ *                                     (natural-log units); empty = -inf
+ *   l  [batch, heads, rows]           running sum of exp(score - m); empty = 0
+ *   o  [batch, heads, rows, head_dim] unnormalised output; empty = 0
+ * batch, heads, rows >= 0 (0 = empty, every call is then a no-op returning
+ * RA_OK); head_dim is 64 or 128.
+ */
+typedef struct {
+  int32_t batch, heads, rows, head_dim;
+  float *m;
+  float *l;
+  float *o;
+} ra_state;
+
+/*
+ * Set the state to the empty state (m = -inf, l = 0, O = 0), the identity of
+ * the merge ("Ring Attention Math Deep", section "Accumulation math, step by
+ * step"; aicassindra architecture article, section "End-to-end flow").
+ * Implemented with a fill kernel, never hipMemset, so it can be captured.
+ */
+ra_status ra_state_init(ra_state *st, hipStream_t stream);
+
+/*
+ * Host-only causal case test for query block i = q_block against key/value
+ * block j = kv_block of num_blocks contiguous blocks ("Ring Attention：...",
+ * section "Causal Attention 让环不再完全对称"):
+ *   causal == 0            -> RA_CASE_FULL
+ *   causal, j > i          -> RA_CASE_SKIP   (block strictly in the future)
+ *   causal, j == i         -> RA_CASE_DIAG   (key t visible to query r iff t <= r)
+ *   causal, j < i          -> RA_CASE_FULL
+ * Returns the case (>= 0) or RA_ERR_INVALID_ARG unless 0 <= i, j < num_blocks
+ * and causal is 0 or 1.  Enqueues nothing; needs no GPU.
+ */
+int32_t ra_step_case(int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal);
+
+/*
+ * Fold one visiting key/value block into the state ("Ring Attention Paper
+ * Breakdown ...", section 3, steps 1-7; the FlashAttention_Update of its
+ * section 2):
+ *   S = scale * Q_i K_j^T  (masked per ra_step_case), m' = max(m, rowmax S),
+ *   l' = exp(m - m') l + rowsum exp(S - m'),  O' = exp(m - m') O + exp(S - m') V_j.
+ * On return of the kernel the state is again in the canonical form above
+ * (m is the running maximum).
+ *   q, k, v    [batch, heads, rows, head_dim] in in_dtype (RA_BF16 or RA_F32);
+ *              q is the rank's block i, k and v are block j.
+ *   kv_rows    rows of k and v; must equal st->rows (equal blocks), else
+ *              RA_ERR_UNSUPPORTED.
+ *   q_block, kv_block, num_blocks, causal   as in ra_step_case; global
+ *              positions are q_block*rows + r and kv_block*rows + t.
+ *   scale      score multiplier, finite and > 0 (1/sqrt(head_dim) normally).
+ * bf16 inputs use the MFMA path (fp32 accumulation, P rounded to bf16 before
+ * the P V product); f32 inputs use an fp32 path.  A skipped block returns
+ * RA_OK and enqueues nothing, leaving the state bit-identical.
+ */
+ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
+                  int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                  int32_t causal, float scale, hipStream_t stream);
+
+/*
+ * dst <- dst (+) src: merge two partial states over disjoint key sets
+ * (aicassindra architecture article, section "The architecture: every piece
+ * explained": take the larger maximum, rescale each side by exp(its max - new
+ * max), add).  Shapes must match.  A row empty on one side takes the other
+ * side's values bit-exactly.  dst and src must not alias.
+ */
+ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream);
+
+/*
+ * Final division and log-sum-exp ("Ring Attention Math Deep", section
+ * "Accumulation math, step by step": out = o / l; "Ring Attention：...",
+ * section "Backward 需要让梯度也沿环传播": the per-row log-sum-exp kept for the
+ * backward).
+ *   o_out   [batch, heads, rows, head_dim] in out_dtype (RA_F32 or RA_BF16,
+ *           round to nearest even); may be NULL to skip.
+ *   lse_out [batch, heads, rows] fp32, = m + ln l; may be NULL to skip.
+ * A row with l == 0 gives o_out = 0 and lse_out = -inf.  The state is not
+ * modified, so more blocks may be folded in afterwards.
+ */
+ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float *lse_out,
+                      hipStream_t stream);
+
+/*
+ * Stage a block: asynchronous device-to-device copy of `bytes` bytes from src
+ * to dst on `stream`.  On one GPU this stands in for the receive of the next
+ * key/value block from the previous rank into the free buffer ("Ring Attention
+ * Paper Breakdown ...", section 2: receive into buffer B while buffer A is
+ * computed on, then swap).  bytes == 0 is a no-op; otherwise both pointers must
+ * be non-NULL and the ranges must not overlap.
+ */
+ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream);
+
+/* Static string naming a status code. */
+const char *ra_status_string(ra_status s);
+
+/* Thread-local detail of the last non-OK return on the calling thread ("" if
+ * none).  Valid until the next library call on this thread. */
+const char *ra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H_ */

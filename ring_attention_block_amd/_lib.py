@@ -1,0 +1,168 @@
+"""ctypes binding of the C ABI in include/ra.h (argument marshalling only).
+
+Torch tensors supply device pointers (``data_ptr()``) and HIP stream handles
+(``torch.cuda.Stream.cuda_stream``); every step of the path runs in libra.so.
+The library is loaded on first use from this package directory; if it is
+missing the call raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
+
+RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, -1, -2, -3
+RA_F32, RA_BF16 = 0, 1
+RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
+
+# Every symbol include/ra.h declares.
+EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_lse_merge", "ra_finalize",
+           "ra_stage_block", "ra_status_string", "ra_last_error")
+
+
+class RaState(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("rows", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+                ("o", ctypes.c_void_p)]
+
+
+class RaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_status_name(status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libra.so (loads it on first call)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m ring_attention_block_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        sp = ctypes.POINTER(RaState)
+        sig = {
+            "ra_state_init": (ctypes.c_int, [sp, vp]),
+            "ra_step_case": (i32, [i32, i32, i32, i32]),
+            "ra_step": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp]),
+            "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
+            "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
+            "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
+            "ra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "ra_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _status_name(s: int) -> str:
+    return lib().ra_status_string(s).decode()
+
+
+def last_error() -> str:
+    return lib().ra_last_error().decode()
+
+
+def _check(status: int) -> int:
+    if status < 0:
+        raise RaError(status, last_error())
+    return status
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+class State:
+    """Caller-owned running state (m, l, O) as fp32 torch tensors.
+
+    m, l: [batch, heads, rows]; o: [batch, heads, rows, head_dim].
+    """
+
+    def __init__(self, batch: int, heads: int, rows: int, head_dim: int, device="cuda"):
+        self.m = torch.empty((batch, heads, rows), dtype=torch.float32, device=device)
+        self.l = torch.empty((batch, heads, rows), dtype=torch.float32, device=device)
+        self.o = torch.empty((batch, heads, rows, head_dim), dtype=torch.float32, device=device)
+        self.c = RaState(batch, heads, rows, head_dim, self.m.data_ptr(), self.l.data_ptr(),
+                         self.o.data_ptr())
+
+    @property
+    def shape(self):
+        return (self.c.batch, self.c.heads, self.c.rows, self.c.head_dim)
+
+
+def step_case(q_block: int, kv_block: int, num_blocks: int, causal: bool) -> int:
+    return _check(lib().ra_step_case(q_block, kv_block, num_blocks, int(causal)))
+
+
+def state_init(st: State, stream=None) -> None:
+    _check(lib().ra_state_init(ctypes.byref(st.c), _stream(stream)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return RA_BF16
+    if t.dtype == torch.float32:
+        return RA_F32
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
+         scale: float, stream=None) -> int:
+    """Fold block kv_block into st; returns the causal case (0 skip, 1 diag, 2 full)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    if q.shape != k.shape or k.shape != v.shape:
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if tuple(q.shape) != st.shape:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match the state {st.shape}")
+    _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                         k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
+                         _stream(stream)))
+    return step_case(q_block, kv_block, num_blocks, causal)
+
+
+def lse_merge(dst: State, src: State, stream=None) -> None:
+    _check(lib().ra_lse_merge(ctypes.byref(dst.c), ctypes.byref(src.c), _stream(stream)))
+
+
+def finalize(st: State, out_dtype=torch.float32, stream=None, o_out=None, lse_out=None):
+    """Return (O [B,H,rows,d] in out_dtype, LSE [B,H,rows] fp32)."""
+    b, h, r, d = st.shape
+    if o_out is None:
+        o_out = torch.empty((b, h, r, d), dtype=out_dtype, device=st.o.device)
+    if lse_out is None:
+        lse_out = torch.empty((b, h, r), dtype=torch.float32, device=st.o.device)
+    code = RA_BF16 if o_out.dtype == torch.bfloat16 else RA_F32
+    if o_out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported output dtype {o_out.dtype}")
+    _check(lib().ra_finalize(ctypes.byref(st.c), _ptr(o_out), code, _ptr(lse_out), _stream(stream)))
+    return o_out, lse_out
+
+
+def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+        raise ValueError("stage_block: sizes differ")
+    _check(lib().ra_stage_block(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
+                                _stream(stream)))

@@ -1,0 +1,72 @@
+"""Build libra.so in-tree with hipcc for gfx950.
+
+    python -m ring_attention_block_amd.build [--verbose]
+
+Each HIP source is compiled to an object under _build/ (in parallel), then
+linked into ring_attention_block_amd/libra.so next to this file.  Always
+rebuilds: the caller asked for a build.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libra.so")
+ARCH = "gfx950"
+
+SOURCES = ["ra_host.hip", "ra_state.hip", "ra_step_f32.hip", "ra_step_bf16.hip"]
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-I", os.path.join(ROOT, "include"),
+    # Packed fp32 ops are kept out of every kernel.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libra.so")
+    return path
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(x for x in (r.stdout + r.stderr).splitlines() if noise not in x)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    if msgs.strip() and verbose:
+        print(msgs)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="--verbose" in sys.argv))

@@ -1,0 +1,188 @@
+// C ABI of the ring-step library: argument checks, causal case selection and
+// kernel dispatch.  Nothing here allocates or synchronises; every check runs
+// before anything is enqueued, so a rejected call leaves the state untouched.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/ra.h"
+#include "ra_kernels.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+ra_status fail(ra_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ra_status ok() {
+  g_err[0] = '\0';
+  return RA_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Rows of a state (batch * heads * rows) or -1 on a malformed shape.
+ra_status check_state(const ra_state *st, const char *name, int64_t *n_rows) {
+  if (!st) return fail(RA_ERR_INVALID_ARG, "%s: state pointer is NULL", name);
+  if (st->batch < 0 || st->heads < 0 || st->rows < 0)
+    return fail(RA_ERR_INVALID_ARG, "%s: negative shape (batch=%d heads=%d rows=%d)", name,
+                st->batch, st->heads, st->rows);
+  if (st->head_dim <= 0)
+    return fail(RA_ERR_INVALID_ARG, "%s: head_dim=%d must be positive", name, st->head_dim);
+  if (st->head_dim != 64 && st->head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", name, st->head_dim);
+  const int64_t bh = (int64_t)st->batch * st->heads;
+  if (bh > INT32_MAX) return fail(RA_ERR_INVALID_ARG, "%s: batch*heads exceeds 2^31-1", name);
+  const int64_t n = bh * st->rows;
+  if (n > ((int64_t)1 << 40) / st->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: state of %lld rows is too large", name, (long long)n);
+  if (n > 0) {
+    if (!st->m || !st->l || !st->o)
+      return fail(RA_ERR_INVALID_ARG, "%s: NULL m, l or o with %lld rows", name, (long long)n);
+    if (!aligned16(st->m) || !aligned16(st->l) || !aligned16(st->o))
+      return fail(RA_ERR_INVALID_ARG, "%s: m, l and o must be 16-byte aligned", name);
+  }
+  *n_rows = n;
+  return RA_OK;
+}
+
+ra_status hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess)
+    return fail(RA_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ra_status_string(ra_status s) {
+  switch (s) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_INVALID_ARG: return "RA_ERR_INVALID_ARG";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+  }
+  return "RA_UNKNOWN_STATUS";
+}
+
+const char *ra_last_error(void) { return g_err; }
+
+int32_t ra_step_case(int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal) {
+  if (num_blocks < 1) return fail(RA_ERR_INVALID_ARG, "num_blocks=%d must be >= 1", num_blocks);
+  if (q_block < 0 || q_block >= num_blocks || kv_block < 0 || kv_block >= num_blocks)
+    return fail(RA_ERR_INVALID_ARG, "block indices (q_block=%d, kv_block=%d) outside [0, %d)",
+                q_block, kv_block, num_blocks);
+  if (causal != 0 && causal != 1)
+    return fail(RA_ERR_INVALID_ARG, "causal=%d must be 0 or 1", causal);
+  if (!causal) return RA_CASE_FULL;
+  if (kv_block > q_block) return RA_CASE_SKIP;
+  if (kv_block == q_block) return RA_CASE_DIAG;
+  return RA_CASE_FULL;
+}
+
+ra_status ra_state_init(ra_state *st, hipStream_t stream) {
+  int64_t n = 0;
+  ra_status s = check_state(st, "ra_state_init", &n);
+  if (s != RA_OK) return s;
+  if (n == 0) return ok();
+  (void)hipGetLastError();
+  return hip_status(ra::launch_state_init(st->m, st->l, st->o, n, st->head_dim, stream),
+                    "ra_state_init launch");
+}
+
+ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
+                  int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                  int32_t causal, float scale, hipStream_t stream) {
+  int64_t n = 0;
+  ra_status s = check_state(st, "ra_step", &n);
+  if (s != RA_OK) return s;
+  const int32_t c = ra_step_case(q_block, kv_block, num_blocks, causal);
+  if (c < 0) return (ra_status)c;
+  if (in_dtype != RA_F32 && in_dtype != RA_BF16)
+    return fail(RA_ERR_INVALID_ARG, "ra_step: in_dtype=%d is not RA_F32 or RA_BF16", (int)in_dtype);
+  if (kv_rows < 0) return fail(RA_ERR_INVALID_ARG, "ra_step: kv_rows=%d is negative", kv_rows);
+  if (kv_rows != st->rows)
+    return fail(RA_ERR_UNSUPPORTED, "ra_step: kv_rows=%d differs from rows=%d (equal blocks only)",
+                kv_rows, st->rows);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(RA_ERR_INVALID_ARG, "ra_step: scale=%g must be finite and > 0", (double)scale);
+  if (n > 0) {
+    if (!q || !k || !v) return fail(RA_ERR_INVALID_ARG, "ra_step: NULL q, k or v");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+      return fail(RA_ERR_INVALID_ARG, "ra_step: q, k and v must be 16-byte aligned");
+  }
+  if (c == RA_CASE_SKIP || n == 0) return ok();  // future block / empty: nothing to fold
+
+  ra::StepArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.m = st->m;
+  a.l = st->l;
+  a.o = st->o;
+  a.rows = st->rows;
+  a.bh = st->batch * st->heads;
+  a.scale_log2 = scale * 1.442695040888963407f;
+  const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
+  (void)hipGetLastError();
+  const hipError_t e = in_dtype == RA_BF16 ? ra::launch_step_bf16(a, st->head_dim, sc, stream)
+                                           : ra::launch_step_f32(a, st->head_dim, sc, stream);
+  return hip_status(e, "ra_step launch");
+}
+
+ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream) {
+  int64_t nd = 0, ns = 0;
+  ra_status s = check_state(dst, "ra_lse_merge dst", &nd);
+  if (s != RA_OK) return s;
+  s = check_state(src, "ra_lse_merge src", &ns);
+  if (s != RA_OK) return s;
+  if (dst->batch != src->batch || dst->heads != src->heads || dst->rows != src->rows ||
+      dst->head_dim != src->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: dst and src shapes differ");
+  if (nd == 0) return ok();
+  if (dst->m == src->m || dst->l == src->l || dst->o == src->o)
+    return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: dst and src alias");
+  (void)hipGetLastError();
+  return hip_status(ra::launch_state_merge(dst->m, dst->l, dst->o, src->m, src->l, src->o, nd,
+                                           dst->head_dim, stream),
+                    "ra_lse_merge launch");
+}
+
+ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float *lse_out,
+                      hipStream_t stream) {
+  int64_t n = 0;
+  ra_status s = check_state(st, "ra_finalize", &n);
+  if (s != RA_OK) return s;
+  if (out_dtype != RA_F32 && out_dtype != RA_BF16)
+    return fail(RA_ERR_INVALID_ARG, "ra_finalize: out_dtype=%d is not RA_F32 or RA_BF16",
+                (int)out_dtype);
+  if (n == 0 || (!o_out && !lse_out)) return ok();
+  if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
+    return fail(RA_ERR_INVALID_ARG, "ra_finalize: outputs must be 16-byte aligned");
+  (void)hipGetLastError();
+  return hip_status(ra::launch_finalize(st->m, st->l, st->o, o_out, out_dtype == RA_BF16,
+                                        lse_out, n, st->head_dim, stream),
+                    "ra_finalize launch");
+}
+
+ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return ok();
+  if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "ra_stage_block: NULL pointer");
+  const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
+  if (d < s + bytes && s < d + bytes)
+    return fail(RA_ERR_INVALID_ARG, "ra_stage_block: source and destination overlap");
+  return hip_status(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream),
+                    "ra_stage_block copy");
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal launchers shared by the C-ABI layer (ra_host.hip) and the kernel
+// translation units.  Callers have validated every argument; launchers only
+// enqueue and return the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+// Arguments of one ring-step kernel launch.  Tensors are [bh, rows, D].
+struct StepArgs {
+  const void *q, *k, *v;  // bf16 (uint16 storage) or fp32, per launcher
+  float *m, *l, *o;       // state
+  int32_t rows;           // query rows == key rows of the block
+  int32_t bh;             // batch * heads
+  float scale_log2;       // score scale * log2(e): kernels work in base 2
+};
+
+enum class StepCase : int { Diag = 1, Full = 2 };
+
+hipError_t launch_state_init(float *m, float *l, float *o, int64_t n_rows, int d,
+                             hipStream_t s);
+hipError_t launch_state_merge(float *dm, float *dl, float *dO, const float *sm, const float *sl,
+                              const float *sO, int64_t n_rows, int d, hipStream_t s);
+hipError_t launch_finalize(const float *m, const float *l, const float *o, void *o_out,
+                           bool out_bf16, float *lse, int64_t n_rows, int d, hipStream_t s);
+hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s);
+hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,121 @@
+// fp32 ring-step kernel: fold one fp32 key/value block into the state.
+//
+// Plain fp32 arithmetic (no matrix cores) for small fp32 workloads where the
+// tolerance is 1e-5.  A workgroup owns 64 query rows of one (batch, head);
+// four lanes share a row and each holds a quarter of the row's q and O.  Key
+// and value tiles of 64 rows are staged through LDS.  The state is kept in the
+// canonical form after every tile (m is the running maximum).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "ra_kernels.h"
+
+namespace ra {
+namespace {
+
+constexpr int kRows = 64;     // query rows per workgroup
+constexpr int kKeys = 64;     // keys per LDS tile
+constexpr int kThreads = 256; // 4 lanes per query row
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+template <int D, bool kDiag>
+__global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
+  constexpr int kPart = D / 4;  // columns per lane
+  __shared__ float ks[kKeys][D];
+  __shared__ float vs[kKeys][D];
+
+  const int rows = a.rows;
+  const int n_qt = (rows + kRows - 1) / kRows;
+  const int bh = blockIdx.x / n_qt;
+  const int qt = blockIdx.x % n_qt;
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, part = tid & 3;
+  const int row = qt * kRows + r;
+  const bool row_ok = row < rows;
+  const size_t base = (size_t)bh * rows * D;
+  const float *__restrict__ Q = static_cast<const float *>(a.q) + base;
+  const float *__restrict__ K = static_cast<const float *>(a.k) + base;
+  const float *__restrict__ V = static_cast<const float *>(a.v) + base;
+  float *__restrict__ O = a.o + base;
+  const size_t srow = (size_t)bh * rows + row;
+
+  float qv[kPart], ov[kPart];
+#pragma unroll
+  for (int x = 0; x < kPart; ++x) {
+    qv[x] = row_ok ? Q[(size_t)row * D + part * kPart + x] : 0.f;
+    ov[x] = row_ok ? O[(size_t)row * D + part * kPart + x] : 0.f;
+  }
+  float m2 = row_ok ? a.m[srow] * kLog2e : -INFINITY;  // base-2 running max
+  float l = row_ok ? a.l[srow] : 0.f;
+
+  const int kv_end = kDiag ? min(rows, (qt + 1) * kRows) : rows;
+  for (int k0 = 0; k0 < kv_end; k0 += kKeys) {
+    __syncthreads();
+    for (int e = tid; e < kKeys * D; e += kThreads) {
+      const int kr = e / D, kc = e % D;
+      const bool ok = k0 + kr < rows;
+      ks[kr][kc] = ok ? K[(size_t)(k0 + kr) * D + kc] : 0.f;
+      vs[kr][kc] = ok ? V[(size_t)(k0 + kr) * D + kc] : 0.f;
+    }
+    __syncthreads();
+
+    float s[kKeys];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kKeys; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int x = 0; x < kPart; ++x) acc = fmaf(qv[x], ks[j][part * kPart + x], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      const int key = k0 + j;
+      const bool ok = key < rows && (!kDiag || key <= row);
+      s[j] = ok ? acc : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float mt = mx * a.scale_log2;
+    const float mn = fmaxf(m2, mt);
+    if (mn == -INFINITY) continue;  // nothing visible yet: state unchanged
+    const float alpha = (m2 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+    l *= alpha;
+#pragma unroll
+    for (int x = 0; x < kPart; ++x) ov[x] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kKeys; ++j) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[j], a.scale_log2, -mn));
+      l += p;
+#pragma unroll
+      for (int x = 0; x < kPart; ++x) ov[x] = fmaf(p, vs[j][part * kPart + x], ov[x]);
+    }
+    m2 = mn;
+  }
+
+  if (row_ok) {
+#pragma unroll
+    for (int x = 0; x < kPart; ++x) O[(size_t)row * D + part * kPart + x] = ov[x];
+    if (part == 0) {
+      a.m[srow] = m2 * kLn2;
+      a.l[srow] = l;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s) {
+  const int n_qt = (a.rows + kRows - 1) / kRows;
+  const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(kThreads);
+  const bool diag = c == StepCase::Diag;
+  if (d == 128) {
+    if (diag) step_f32_kernel<128, true><<<grid, block, 0, s>>>(a);
+    else step_f32_kernel<128, false><<<grid, block, 0, s>>>(a);
+  } else {
+    if (diag) step_f32_kernel<64, true><<<grid, block, 0, s>>>(a);
+    else step_f32_kernel<64, false><<<grid, block, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ra

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before enqueuing."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ring_attention_block_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ra.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ra_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libra.so is not built (python -m ring_attention_block_amd.build)")
+    return _lib.lib()
+
+
+def test_header_matches_binding_exports():
+    assert _declared() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert L.ra_status_string(0) == b"RA_OK"
+    assert L.ra_status_string(-1) == b"RA_ERR_INVALID_ARG"
+    assert L.ra_status_string(-2) == b"RA_ERR_UNSUPPORTED"
+    assert L.ra_status_string(-3) == b"RA_ERR_HIP"
+
+
+@pytest.mark.parametrize("P", [1, 2, 5, 8])
+def test_step_case_table(L, P):
+    for i in range(P):
+        for j in range(P):
+            assert L.ra_step_case(i, j, P, 0) == _lib.RA_CASE_FULL
+            want = _lib.RA_CASE_SKIP if j > i else (_lib.RA_CASE_DIAG if j == i else _lib.RA_CASE_FULL)
+            assert L.ra_step_case(i, j, P, 1) == want
+
+
+def test_step_case_rejects(L):
+    assert L.ra_step_case(0, 0, 0, 1) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_step_case(3, 0, 3, 1) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_step_case(0, -1, 3, 1) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_step_case(0, 0, 3, 2) == _lib.RA_ERR_INVALID_ARG
+    assert b"causal" in L.ra_last_error()
+
+
+FAKE = 1 << 20   # an aligned non-NULL address; never dereferenced by a rejected call
+
+
+def _state(rows=128, d=128, m=FAKE, l=FAKE, o=FAKE, batch=1, heads=2):
+    return _lib.RaState(batch, heads, rows, d, m, l, o)
+
+
+def _step(L, st, q=FAKE, k=FAKE, v=FAKE, dtype=_lib.RA_BF16, kv_rows=None, i=1, j=0, P=2,
+          causal=1, scale=0.125):
+    kv = st.rows if kv_rows is None else kv_rows
+    return L.ra_step(ctypes.byref(st), q, k, v, dtype, kv, i, j, P, causal, scale, None)
+
+
+def test_step_rejects_before_enqueue(L):
+    st = _state()
+    assert L.ra_step(None, FAKE, FAKE, FAKE, 1, 128, 1, 0, 2, 1, 0.1, None) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, _state(d=96)) == _lib.RA_ERR_UNSUPPORTED
+    assert b"head_dim" in L.ra_last_error()
+    assert _step(L, _state(d=0)) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, _state(rows=-1)) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, kv_rows=64) == _lib.RA_ERR_UNSUPPORTED
+    assert _step(L, st, i=2, P=2) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, j=-1) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, causal=3) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, dtype=7) == _lib.RA_ERR_INVALID_ARG
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert _step(L, st, scale=bad) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, q=0) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, v=FAKE + 8) == _lib.RA_ERR_INVALID_ARG
+    assert b"aligned" in L.ra_last_error()
+    assert _step(L, _state(m=0)) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, _state(o=FAKE + 4)) == _lib.RA_ERR_INVALID_ARG
+
+
+def test_skip_and_empty_enqueue_nothing(L):
+    # A causal future block and an empty state return OK without any HIP call,
+    # so they succeed even where no GPU exists.
+    assert _step(L, _state(), i=0, j=1, P=2) == _lib.RA_OK
+    assert L.ra_last_error() == b""
+    empty = _state(rows=0, m=0, l=0, o=0)
+    assert _step(L, empty, q=0, k=0, v=0) == _lib.RA_OK
+    assert L.ra_state_init(ctypes.byref(empty), None) == _lib.RA_OK
+    assert L.ra_finalize(ctypes.byref(empty), None, 0, None, None) == _lib.RA_OK
+    assert L.ra_lse_merge(ctypes.byref(empty), ctypes.byref(_state(rows=0, m=0, l=0, o=0)), None) == 0
+    assert L.ra_stage_block(None, None, 0, None) == _lib.RA_OK
+
+
+def test_merge_finalize_stage_reject(L):
+    a, b = _state(), _state(rows=64)
+    assert L.ra_lse_merge(ctypes.byref(a), ctypes.byref(b), None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_lse_merge(ctypes.byref(a), ctypes.byref(_state()), None) == _lib.RA_ERR_INVALID_ARG
+    assert b"alias" in L.ra_last_error()
+    assert L.ra_lse_merge(None, ctypes.byref(a), None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_finalize(ctypes.byref(a), FAKE, 5, None, None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_finalize(ctypes.byref(a), FAKE + 2, 0, None, None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_stage_block(FAKE, None, 16, None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_stage_block(FAKE, FAKE + 8, 16, None) == _lib.RA_ERR_INVALID_ARG
+    assert b"overlap" in L.ra_last_error()
+    assert L.ra_state_init(None, None) == _lib.RA_ERR_INVALID_ARG
