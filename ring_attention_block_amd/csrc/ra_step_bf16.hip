@@ -70,17 +70,29 @@ struct Tile {
   static constexpr int kChunks = D / 8;                   // 16-byte chunks per row
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;   // rows per wavefront load
   static constexpr int kLoads = kBytes / 1024;            // wavefront loads per tile
-  static constexpr int kBufBytes = 2 * kBytes;            // K then V
-  static constexpr size_t kLdsBytes = 2 * kBufBytes;      // double buffered
+  static constexpr size_t kLdsBytes = 4 * kBytes;          // K and V, double buffered
 };
 
 // Key held by LDS row rho of the K tile: bits 2 and 3 swapped within 32.
 __device__ __forceinline__ int k_row_key(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 }
-// 16-byte chunk swizzles of the K and V tiles.
-__device__ __forceinline__ int k_swz(int rho) { return rho & 7; }
-__device__ __forceinline__ int v_swz(int rho) { return 2 * (rho & 3); }
+// 16-byte chunk swizzles of the K and V tiles.  The fragment reads are
+// conflict-free whether the LDS serves a 16-byte read in passes of 8 lanes
+// over 32 banks or of 16 lanes over 64 banks (and an 8-byte read in passes of
+// 16 or 32 lanes): K reads take 8/16 consecutive rows at one logical chunk;
+// a transposed V read takes 4 consecutive rows at 32/64 contiguous bytes.
+template <int D>
+__device__ __forceinline__ int k_swz(int rho) {
+  if constexpr (D == 128) return rho & 15;
+  else return (rho & 7) ^ ((rho >> 3) & 1);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int rho) {
+  const int x = rho & 3;
+  if constexpr (D == 128) return 4 * x + 2 * ((x ^ (x >> 1)) & 1);   // 0, 6, 10, 12
+  else return 2 * x;
+}
 
 // Device-only helpers (the buffer resource type exists only for the GPU target).
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -104,43 +116,42 @@ __device__ __forceinline__ Stage<D, kW> stage_offsets(int wave, int lane) {
     const int n = wave + i * kW;
     const int rho = n * T::kRowsPerLoad + lane / T::kChunks;
     const int chi = lane % T::kChunks;
-    so.k[i] = (uint32_t)(k_row_key(rho) * T::kRowBytes + ((chi ^ k_swz(rho)) * 16));
-    so.v[i] = (uint32_t)(rho * T::kRowBytes + ((chi ^ v_swz(rho)) * 16));
+    so.k[i] = (uint32_t)(k_row_key(rho) * T::kRowBytes + ((chi ^ k_swz<D>(rho)) * 16));
+    so.v[i] = (uint32_t)(rho * T::kRowBytes + ((chi ^ v_swz<D>(rho)) * 16));
   }
   return so;
 }
 
-// Issue this wavefront's share of the HBM -> LDS copies of the tile at key k0.
+// Issue this wavefront's share of the HBM -> LDS copies of one K (or V) tile
+// starting at key k0 into `buf`.  The tile offset goes into the per-lane
+// offset, which the buffer range check covers (the scalar offset is not range
+// checked).
 template <int D, int kW>
-__device__ __forceinline__ void issue_tile(char *buf, __amdgpu_buffer_rsrc_t rk,
-                                           __amdgpu_buffer_rsrc_t rv, const Stage<D, kW> &so,
-                                           int k0, int wave) {
+__device__ __forceinline__ void issue_copy(char *buf, __amdgpu_buffer_rsrc_t rsrc,
+                                           const uint32_t (&off)[Stage<D, kW>::kPerWave], int k0,
+                                           int wave) {
   using T = Tile<D>;
-  // The tile offset goes into the per-lane offset, which the buffer range
-  // check covers (the scalar offset is not range checked).
   const uint32_t toff = (uint32_t)k0 * T::kRowBytes;
 #pragma unroll
   for (int i = 0; i < Stage<D, kW>::kPerWave; ++i) {
     const int n = wave + i * kW;
-    if (Stage<D, kW>::kPerWave * kW == T::kLoads || n < T::kLoads) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void *)(buf + n * 1024), 16, so.k[i] + toff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void *)(buf + T::kBytes + n * 1024), 16,
-                                               so.v[i] + toff, 0, 0, 0);
-    }
+    if (Stage<D, kW>::kPerWave * kW == T::kLoads || n < T::kLoads)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)(buf + n * 1024), 16, off[i] + toff, 0,
+                                               0, 0);
   }
 }
 
-// Zero the LDS rows of a tile buffer whose keys lie at or past `n_valid` (only
-// for the last tile of a block whose length is not a multiple of 64).  These
-// rows are disjoint from the rows the copies write.
+// Zero the LDS rows of a K and a V tile buffer whose keys lie at or past
+// `n_valid` (only for the last tile of a block whose length is not a multiple
+// of 64).  These rows are disjoint from the rows the copies write.
 template <int D, int kW>
-__device__ __forceinline__ void zero_tail(char *buf, int n_valid, int tid) {
+__device__ __forceinline__ void zero_tail(char *kbuf, char *vbuf, int n_valid, int tid) {
   using T = Tile<D>;
   for (int e = tid; e < kBN * T::kChunks; e += 64 * kW) {
     const int rho = e / T::kChunks, chi = e % T::kChunks;
     const uint4 z = make_uint4(0, 0, 0, 0);
-    if (k_row_key(rho) >= n_valid) *reinterpret_cast<uint4 *>(buf + rho * T::kRowBytes + chi * 16) = z;
-    if (rho >= n_valid) *reinterpret_cast<uint4 *>(buf + T::kBytes + rho * T::kRowBytes + chi * 16) = z;
+    if (k_row_key(rho) >= n_valid) *reinterpret_cast<uint4 *>(kbuf + rho * T::kRowBytes + chi * 16) = z;
+    if (rho >= n_valid) *reinterpret_cast<uint4 *>(vbuf + rho * T::kRowBytes + chi * 16) = z;
   }
 }
 
@@ -177,26 +188,35 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key_base, int lim)
     }
 }
 
-// Updates the row state and produces P as four bf16 B-operand fragments.
-// Returns the O rescale factor; `rescale` is set when any lane of the
-// wavefront needs it.
-__device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], RowState &rs, bf16x8 (&pb)[4],
-                                              float sl2, bool &rescale) {
-  float mx = -INFINITY;
+// Row maximum of a score tile and the lazy-rescale decision.  `valid` false
+// leaves the state untouched (a tile past the block end).  Updates the
+// reference and true maxima, scales the partial row sum, and returns the
+// factor the O accumulator must be scaled by; `rescale` is set when any lane
+// of the wavefront needs it.
+__device__ __forceinline__ float tile_max_update(const f32x16 (&s)[2], RowState &rs, float sl2,
+                                                 bool valid, bool &rescale) {
+  float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[1][0], s[1][1]);   // two chains
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-  mx = half_swap_max(mx);
-  const float mt = mx * sl2;
-  rs.m_run = fmaxf(rs.m_run, mt);
-  const bool need = mt > rs.m_ref + kTau;
+  for (int i = 2; i < 16; ++i) {
+    m0 = fmaxf(m0, s[0][i]);
+    m1 = fmaxf(m1, s[1][i]);
+  }
+  const float mt = half_swap_max(fmaxf(m0, m1)) * sl2;
+  rs.m_run = valid ? fmaxf(rs.m_run, mt) : rs.m_run;
+  const bool need = valid && mt > rs.m_ref + kTau;
   const float m_new = need ? mt : rs.m_ref;
   const float alpha = need ? __builtin_amdgcn_exp2f(rs.m_ref - m_new) : 1.f;
   rescale = __any(need);
   rs.m_ref = m_new;
   rs.l *= alpha;
-  const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+  return alpha;
+}
+
+// P = exp2(s * scale*log2(e) - m_ref) as four bf16 B-operand fragments, and
+// the partial row sum of the fp32 values.
+__device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], RowState &rs, bf16x8 (&pb)[4],
+                                         float sl2) {
+  const float neg_m = (rs.m_ref == -INFINITY) ? 0.f : -rs.m_ref;
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};   // four independent add chains
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
@@ -209,17 +229,25 @@ __device__ __forceinline__ float softmax_tile(const f32x16 (&s)[2], RowState &rs
         pb[sb * 2 + half][j] = (__bf16)p;
       }
   rs.l += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
-  return alpha;
 }
 
-template <int D, bool kDiag, int kW>
+// kMask: some tile may need the element mask (diagonal block, or a block
+// length that is not a multiple of 64).
+template <int D, bool kDiag, int kW, bool kMask>
 __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D>;
   constexpr int kBM = 32 * kW;  // query rows per workgroup
   constexpr int kQK = D / 16;   // k-chunks of the score product
   constexpr int kDB = D / 32;   // 32-row blocks of O^T
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // Four separate LDS objects (K and V, double buffered).  Being distinct
+  // objects lets the compiler see that the HBM->LDS copies into one buffer do
+  // not alias the reads of the other, so it does not make every LDS read wait
+  // for the copies still in flight.
+  __shared__ __attribute__((aligned(1024))) char lds_k0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[T::kBytes];
 
   const int rows = a.rows;
   const int n_qt = (rows + kBM - 1) / kBM;
@@ -259,14 +287,18 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
 
   const int kv_end = kDiag ? min(rows, qt * kBM + kBM) : rows;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
-  // A ragged last tile that is the first use of its LDS buffer must not see
-  // uninitialised LDS past the block end: zero those rows.  A later buffer
-  // use holds finite keys/values of an earlier full tile there, which the
+  // Tile n uses K and V buffer n % 2.
+
+  // A ragged last tile that is the first use of its LDS buffers must not see
+  // uninitialised LDS past the block end: zero those rows.  A later use of a
+  // buffer holds finite keys/values of an earlier full tile there, which the
   // mask (keys) and the zero probabilities (values) already neutralise.
   const int last = n_tiles - 1;
   if (last <= 1 && last * kBN + kBN > rows)
-    zero_tail<D, kW>(lds + (last & 1) * T::kBufBytes, rows - last * kBN, tid);
-  issue_tile<D, kW>(lds, rk, rv, so, 0, wave);
+    zero_tail<D, kW>((last & 1) ? lds_k1 : lds_k0, (last & 1) ? lds_v1 : lds_v0, rows - last * kBN, tid);
+  issue_copy<D, kW>(lds_k0, rk, so.k, 0, wave);
+  issue_copy<D, kW>(lds_v0, rv, so.v, 0, wave);
+  if (n_tiles > 1) issue_copy<D, kW>(lds_k1, rk, so.k, kBN, wave);
 
   // Q^T fragments: lane (r, h) holds q[row][16c + 8h .. 16c + 8h + 7].
   bf16x8 qf[kQK];
@@ -306,7 +338,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   uint32_t koff[kQK];
 #pragma unroll
   for (int c = 0; c < kQK; ++c)
-    koff[c] = (uint32_t)(r * T::kRowBytes + (((2 * c + h) ^ k_swz(r)) * 16));
+    koff[c] = (uint32_t)(r * T::kRowBytes + (((2 * c + h) ^ k_swz<D>(r)) * 16));
   uint32_t voff[kDB];
   {
     const int g = lane >> 4, j = lane & 15;
@@ -314,58 +346,135 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
 #pragma unroll
     for (int b = 0; b < kDB; ++b) {
       const int chunk = 4 * b + 2 * (g & 1) + ((j & 3) >> 1);
-      voff[b] = (uint32_t)(vrow * T::kRowBytes + ((chunk ^ v_swz(vrow)) * 16) + 8 * (j & 1));
+      voff[b] = (uint32_t)(vrow * T::kRowBytes + ((chunk ^ v_swz<D>(vrow)) * 16) + 8 * (j & 1));
     }
   }
 
   const float sl2 = a.scale_log2;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();   // tile 0 (and a zeroed tail) visible to every wavefront
+  const int lim = kDiag ? min(row, rows - 1) : rows - 1;   // last key this row may see
 
-#pragma clang loop unroll(disable)
-  for (int t = 0; t < n_tiles; ++t) {
-    const int k0 = t * kBN;
-    const char *cur = lds + (t & 1) * T::kBufBytes;
-    if (t + 1 < n_tiles) issue_tile<D, kW>(lds + ((t + 1) & 1) * T::kBufBytes, rk, rv, so, k0 + kBN, wave);
-
-    // Whole tile beyond every row of this wavefront (diagonal only): skip.
-    const bool wave_skip = kDiag && k0 > q0w + 31;
-    const bool need_mask = (kDiag && k0 + kBN - 1 > q0w) || (k0 + kBN > rows);
-    if (!wave_skip) {
-      f32x16 s[2];
+  // S^T = K Q^T for the tile in K buffer `kb`.
+  auto scores = [&](f32x16 (&s)[2], const char *kb) {
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        s[sb] = f32x16{};
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < kQK; ++c) {
-          const bf16x8 kf = *(const lds_bf16x8 *)(cur + sb * 32 * T::kRowBytes + koff[c]);
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[sb], 0, 0, 0);
-        }
+      for (int c = 0; c < kQK; ++c) {
+        const bf16x8 kf = *(const lds_bf16x8 *)(kb + sb * 32 * T::kRowBytes + koff[c]);
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[sb], 0, 0, 0);
       }
-      if (need_mask) mask_tile(s, k0 + h * 8, kDiag ? min(row, rows - 1) : rows - 1);
-      bf16x8 pb[4];
-      bool rescale;
-      const float alpha = softmax_tile(s, rs, pb, sl2, rescale);
-      if (rescale) {
+    }
+  };
+  // V^T fragment (b, c) of the tile in V buffer `vb`: two transposed reads.
+  auto read_v = [&](const char *vb, int c, int b) {
+    const char *p0 = vb + (16 * c) * T::kRowBytes + voff[b];
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p0);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0 + 4 * T::kRowBytes));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // O^T += V^T P^T for the tile in V buffer `vb`.  Key chunk outermost: the
+  // kDB accumulators of one chunk are independent, and the V reads of the
+  // next chunk overlap this chunk's MFMAs.
+  auto accumulate = [&](const bf16x8 (&pb)[4], const char *vb) {
 #pragma unroll
-        for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
-      }
-      const char *vt = cur + T::kBytes;
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int b = 0; b < kDB; ++b)
+        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_v(vb, c, b), pb[c], oacc[b], 0, 0, 0);
+  };
+  // Tile t: nothing for this wavefront (diagonal only: every key after every
+  // row of the wavefront) / needs the element mask.
+  auto skip_tile = [&](int t) { return kDiag && t * kBN > q0w + 31; };
+  auto mask_needed = [&](int t) {
+    return (kDiag && t * kBN + kBN - 1 > q0w) || (t * kBN + kBN > rows);
+  };
+
+  // Software pipeline, one tile ahead.  Iteration t issues the copies of
+  // K(t+2) and V(t+1), and in one branch-free block computes the scores of
+  // tile t+1, the exponentials of tile t, the P V product of tile t and the
+  // row maximum of tile t+1; the rare rescale of O for tile t+1 follows.
+  // K(t+2) reuses the buffer of K(t), read one iteration earlier; V(t+1)
+  // reuses that of V(t-1).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();   // K(0), V(0), K(1) (and a zeroed tail) visible to all
+  f32x16 s_cur[2];
+  {
+    scores(s_cur, lds_k0);   // tile 0 is never skipped
+    if (kMask && mask_needed(0)) mask_tile(s_cur, h * 8, lim);
+    bool rescale;
+    const float alpha = tile_max_update(s_cur, rs, sl2, true, rescale);
+    if (rescale) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const char *p0 = vt + (16 * c) * T::kRowBytes + voff[b];
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p0);
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p0 + 4 * T::kRowBytes));
-          const bf16x8 vf =
-              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], oacc[b], 0, 0, 0);
-        }
+      for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of tile t+1 have landed
-    __syncthreads();
   }
+  __syncthreads();   // every wavefront is done with K buffer 0
+
+  // Iteration t.  The buffers are passed explicitly (unrolled by two below)
+  // so that every LDS access names one static buffer:
+  //   copies: K(t+2) -> k_dst (= K buffer t%2), V(t+1) -> v_dst (V buffer (t+1)%2)
+  //   reads:  K(t+1) <- k_src (K buffer (t+1)%2), V(t) <- v_src (V buffer t%2)
+  auto iteration = [&](int t, char *k_dst, char *v_dst, const char *k_src, const char *v_src) {
+    if (t + 2 < n_tiles) issue_copy<D, kW>(k_dst, rk, so.k, (t + 2) * kBN, wave);
+    if (t + 1 < n_tiles) issue_copy<D, kW>(v_dst, rv, so.v, (t + 1) * kBN, wave);
+    const bool has_next = t + 1 < n_tiles;
+
+    f32x16 s_nxt[2];
+    bf16x8 pb[4];
+    bool rescale = false;
+    float alpha = 1.f;
+    if (!kMask) {
+      // The scores of the tile after the last one read a stale K buffer;
+      // has_next = false keeps them out of the state.
+      scores(s_nxt, k_src);
+      tile_exp(s_cur, rs, pb, sl2);
+      accumulate(pb, v_src);
+      alpha = tile_max_update(s_nxt, rs, sl2, has_next, rescale);
+      // Interleave: per score MFMA one LDS read and six vector instructions
+      // (exponentials of tile t), then per P V MFMA two LDS reads and two
+      // vector instructions (row maximum of tile t+1).
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * kQK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4 * kDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+      }
+    } else {
+      const bool run_next = has_next && !skip_tile(t + 1);
+      if (run_next) scores(s_nxt, k_src);
+      if (!skip_tile(t)) {
+        tile_exp(s_cur, rs, pb, sl2);
+        accumulate(pb, v_src);
+      }
+      if (run_next) {
+        if (mask_needed(t + 1)) mask_tile(s_nxt, (t + 1) * kBN + h * 8, lim);
+        alpha = tile_max_update(s_nxt, rs, sl2, true, rescale);
+      }
+    }
+    if (rescale) {
+#pragma unroll
+      for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) s_cur[sb] = s_nxt[sb];
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of K(t+2), V(t+1) landed
+    __syncthreads();
+  };
+
+  int t = 0;
+#pragma clang loop unroll(disable)
+  for (; t + 1 < n_tiles; t += 2) {
+    iteration(t, lds_k0, lds_v1, lds_k1, lds_v0);
+    iteration(t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+  }
+  if (t < n_tiles) iteration(t, lds_k0, lds_v1, lds_k1, lds_v0);
 
   // ---- back to the canonical state (m = true running maximum) --------------
   const float l_tot = half_swap_sum(rs.l);
@@ -394,7 +503,12 @@ hipError_t launch(const StepArgs &a, hipStream_t s) {
   constexpr int kBM = 32 * kW;
   const int n_qt = (a.rows + kBM - 1) / kBM;
   const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(64 * kW);
-  step_bf16_kernel<D, kDiag, kW><<<grid, block, Tile<D>::kLdsBytes, s>>>(a);
+  if constexpr (kDiag) {
+    step_bf16_kernel<D, true, kW, true><<<grid, block, 0, s>>>(a);
+  } else {
+    if (a.rows % kBN != 0) step_bf16_kernel<D, false, kW, true><<<grid, block, 0, s>>>(a);
+    else step_bf16_kernel<D, false, kW, false><<<grid, block, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
