@@ -147,8 +147,11 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
  * to dst on `stream`.  On one GPU this stands in for the receive of the next
  * key/value block from the previous rank into the free buffer ("Ring Attention
  * Paper Breakdown ...", section 2: receive into buffer B while buffer A is
- * computed on, then swap).  bytes == 0 is a no-op; otherwise both pointers must
- * be non-NULL and the ranges must not overlap.
+ * computed on, then swap).  Runs as a kernel of this library (non-temporal
+ * loads and stores, so it disturbs the cache of a step running beside it as
+ * little as possible).  bytes == 0 is a no-op; otherwise both pointers must be
+ * non-NULL and 16-byte aligned, bytes a multiple of 16, and the ranges must
+ * not overlap.
  */
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream);
 

@@ -181,8 +181,10 @@ ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t s
   const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
   if (d < s + bytes && s < d + bytes)
     return fail(RA_ERR_INVALID_ARG, "ra_stage_block: source and destination overlap");
-  return hip_status(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, stream),
-                    "ra_stage_block copy");
+  if (!aligned16(dst) || !aligned16(src) || bytes % 16 != 0)
+    return fail(RA_ERR_INVALID_ARG, "ra_stage_block: pointers must be 16-byte aligned and bytes a multiple of 16");
+  (void)hipGetLastError();
+  return hip_status(ra::launch_stage_copy(dst, src, bytes, stream), "ra_stage_block launch");
 }
 
 }  // extern "C"

@@ -27,5 +27,7 @@ hipError_t launch_finalize(const float *m, const float *l, const float *o, void 
                            bool out_bf16, float *lse, int64_t n_rows, int d, hipStream_t s);
 hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s);
 hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s);
+// bytes a multiple of 16, both pointers 16-byte aligned, no overlap.
+hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 
 }  // namespace ra

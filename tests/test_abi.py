@@ -115,4 +115,7 @@ def test_merge_finalize_stage_reject(L):
     assert L.ra_stage_block(FAKE, None, 16, None) == _lib.RA_ERR_INVALID_ARG
     assert L.ra_stage_block(FAKE, FAKE + 8, 16, None) == _lib.RA_ERR_INVALID_ARG
     assert b"overlap" in L.ra_last_error()
+    assert L.ra_stage_block(FAKE, FAKE + 4096 + 8, 16, None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_stage_block(FAKE, FAKE + 4096, 24, None) == _lib.RA_ERR_INVALID_ARG
+    assert b"aligned" in L.ra_last_error()
     assert L.ra_state_init(None, None) == _lib.RA_ERR_INVALID_ARG
