@@ -213,22 +213,29 @@ __device__ __forceinline__ float tile_max_update(const f32x16 (&s)[2], RowState 
 }
 
 // P = exp2(s * scale*log2(e) - m_ref) as four bf16 B-operand fragments, and
-// the partial row sum of the fp32 values.
+// the partial row sum of those bf16 values (the same weights the P V product
+// uses), accumulated in fp32 two at a time by v_dot2c_f32_bf16 in two chains.
 __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], RowState &rs, bf16x8 (&pb)[4],
                                          float sl2) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const float neg_m = (rs.m_ref == -INFINITY) ? 0.f : -rs.m_ref;
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};   // four independent add chains
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[sb][half * 8 + j], sl2, neg_m));
-        lsum[j & 3] += p;
-        pb[sb * 2 + half][j] = (__bf16)p;
-      }
-  rs.l += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+      for (int j = 0; j < 8; ++j)
+        pb[sb * 2 + half][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[sb][half * 8 + j], sl2, neg_m));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float acc[2] = {0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    acc[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 0, 1), ones, acc[0], false);
+    acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 2, 3), ones, acc[1], false);
+    acc[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 4, 5), ones, acc[0], false);
+    acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[c], pb[c], 6, 7), ones, acc[1], false);
+  }
+  rs.l += acc[0] + acc[1];
 }
 
 // kMask: some tile may need the element mask (diagonal block, or a block
@@ -430,7 +437,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       tile_exp(s_cur, rs, pb, sl2);
       accumulate(pb, v_src);
       alpha = tile_max_update(s_nxt, rs, sl2, has_next, rescale);
-      // Interleave: per score MFMA one LDS read and six vector instructions
+      // Interleave: per score MFMA one LDS read and four vector instructions
       // (exponentials of tile t), then per P V MFMA two LDS reads and two
       // vector instructions (row maximum of tile t+1).
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -438,7 +445,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       for (int i = 0; i < 2 * kQK; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
       }
 #pragma unroll
       for (int i = 0; i < 4 * kDB; ++i) {
