@@ -14,6 +14,7 @@ per head (the diagonal block counts c(c+1)/2 pairs, skipped blocks none).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -59,6 +60,34 @@ def generate(wl, rank, threads=16):
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         arrs = list(ex.map(lambda rj: synth.block(wl, *rj), jobs))
     return dict(zip(jobs, arrs))
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "ra_step_bf16_full_causal_h32_d128_c4096_hbm_traffic.md")
+
+
+def measured_traffic(wl):
+    """HBM bytes per full-step launch from the committed FETCH_SIZE/WRITE_SIZE summary.
+
+    Only for the workload the counters were taken on, and only while the
+    kernel source still hashes to the value recorded with them; else None.
+    """
+    if wl.name != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        key, sep, val = line.strip().partition(": ")
+        if sep and key in ("traffic_bytes_per_launch", "kernel_source", "kernel_source_sha256"):
+            fields[key] = val.strip()
+    if len(fields) != 3:
+        return None
+    src = os.path.join(ROOT, fields["kernel_source"])
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, rank, blocks, target_s=15.0):
@@ -188,7 +217,8 @@ def main():
                    "pct_of_mfma_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "kernel": dom,
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(wl) if full else None,
                      "avg_launch_ms": round(dom_ms, 5),
                      "launches": len(full) if full else len(diag),
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},

@@ -147,9 +147,10 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
  * to dst on `stream`.  On one GPU this stands in for the receive of the next
  * key/value block from the previous rank into the free buffer ("Ring Attention
  * Paper Breakdown ...", section 2: receive into buffer B while buffer A is
- * computed on, then swap).  Runs as a kernel of this library (non-temporal
- * loads and stores, so it disturbs the cache of a step running beside it as
- * little as possible).  bytes == 0 is a no-op; otherwise both pointers must be
+ * computed on, then swap).  Runs as a kernel of this library built to run
+ * beside a step: non-temporal loads and stores, and a small grid that leaves
+ * the compute units to the step, so a copy alone is slower than a full-chip
+ * copy but overlaps well.  bytes == 0 is a no-op; otherwise both pointers must be
  * non-NULL and 16-byte aligned, bytes a multiple of 16, and the ranges must
  * not overlap.
  */

@@ -3,10 +3,12 @@
 // Attention Paper Breakdown: Blockwise Distributed Transformers for
 // Near-Infinite Context", section 2: receive into buffer B, then swap).
 //
-// Bound by HBM bandwidth (read + write of every byte).  The loads and stores
-// carry the non-temporal hint: the block is not reused from cache by this
-// copy, and streaming it should disturb the L2 working set of a step kernel
-// running beside it as little as possible.
+// The copy runs beside a step kernel, which it should disturb as little as
+// possible: the loads and stores carry the non-temporal hint (the block is not
+// reused from cache by this copy), and the grid is small (kMaxBlocks
+// workgroups of four wavefronts: one on half of the CUs), so the step kernel's
+// workgroups, which need most of a CU each, still find room on every CU.  The copy then takes a few tens of microseconds for a 32 MiB block,
+// well inside one step.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,6 +21,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
+constexpr int64_t kMaxBlocks = 128;
 
 template <bool kNonTemporal>
 __global__ void __launch_bounds__(kThreads) stage_copy_kernel(u32x4 *__restrict__ dst,
@@ -49,7 +52,7 @@ __global__ void __launch_bounds__(kThreads) stage_copy_kernel(u32x4 *__restrict_
 hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
   const int64_t n16 = (int64_t)(bytes / 16);
   int64_t blocks = (n16 + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
-  if (blocks > 2048) blocks = 2048;
+  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
   if (blocks < 1) blocks = 1;
   stage_copy_kernel<true><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
       static_cast<u32x4 *>(dst), static_cast<const u32x4 *>(src), n16);

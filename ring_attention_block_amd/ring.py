@@ -22,6 +22,7 @@ from typing import Callable, Sequence
 import torch
 
 from . import _lib
+from .hip_events import Event
 
 
 def ring_order(rank: int, blocks: int) -> list:
@@ -42,9 +43,9 @@ class RingEmulator:
                       torch.empty(self.shape, dtype=dtype, device=device)) for _ in range(2)]
         self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
         self.copy = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
-        self.ev_ready = [torch.cuda.Event(), torch.cuda.Event()]
-        self.ev_free = [torch.cuda.Event(), torch.cuda.Event()]
-        self.ev_start = torch.cuda.Event()
+        self.ev_ready = [Event(), Event()]
+        self.ev_free = [Event(), Event()]
+        self.ev_start = Event()
 
     def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
             rank: int, num_blocks: int, causal: bool, scale: float,
@@ -64,7 +65,7 @@ class RingEmulator:
         # Copies of this run start after everything already queued on the
         # compute stream (earlier runs may still read the buffers).
         self.ev_start.record(comp)
-        copy.wait_event(self.ev_start)
+        self.ev_start.wait(copy)
 
         cur = kv_source(order[0])
         cur_buf = None           # index of the buffer `cur` lives in (None: source)
@@ -80,10 +81,10 @@ class RingEmulator:
                 _lib.stage_block(vb, v_src, copy)
                 self.ev_ready[nxt_buf].record(copy)
             if cur_buf is not None:
-                comp.wait_event(self.ev_ready[cur_buf])
+                self.ev_ready[cur_buf].wait(comp)
             case = _lib.step_case(rank, j, num_blocks, causal)
             if step_timers is not None and case != _lib.RA_CASE_SKIP:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = Event(timing=True), Event(timing=True)
                 e0.record(comp)
                 _lib.step(st, q, cur[0], cur[1], rank, j, num_blocks, causal, scale, comp)
                 e1.record(comp)
@@ -98,7 +99,7 @@ class RingEmulator:
                 # the copy stream waits for its free event before refilling it.
                 if cur_buf is not None:
                     free_buf = cur_buf
-                    copy.wait_event(self.ev_free[cur_buf])
+                    self.ev_free[cur_buf].wait(copy)
                 else:
                     free_buf = 1 - nxt_buf
                 cur, cur_buf = self.bufs[nxt_buf], nxt_buf

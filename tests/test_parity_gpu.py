@@ -99,6 +99,10 @@ SMALL = [
     (1, 128, 64, 2, "bf16"),
     (2, 128, 333, 2, "f32"),
     (1, 64, 70, 3, "f32"),
+    # long enough that masked launches run whole tiles before their masked ones
+    (2, 128, 1000, 2, "bf16"),
+    (2, 128, 512, 2, "bf16"),
+    (1, 64, 777, 2, "bf16"),
 ]
 
 
