@@ -320,17 +320,6 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
                        : make_uint4(0, 0, 0, 0);
       qf[c] = __builtin_bit_cast(bf16x8, u);
     }
-#pragma unroll
-    for (int b = 0; b < kDB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 x = row_ok ? *reinterpret_cast<const float4 *>(O + ro + b * 32 + g * 8 + h * 4)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-        oacc[b][4 * g + 0] = x.x;
-        oacc[b][4 * g + 1] = x.y;
-        oacc[b][4 * g + 2] = x.z;
-        oacc[b][4 * g + 3] = x.w;
-      }
     const size_t sr = (size_t)bh * rows + row;
     const float m_state = row_ok ? a.m[sr] * kLog2e : -INFINITY;
     rs.m_ref = m_state;
@@ -404,6 +393,23 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // reuses that of V(t-1).
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();   // K(0), V(0), K(1) (and a zeroed tail) visible to all
+  // The O state is first needed by the P V product of tile 0 (or a rescale):
+  // its loads are issued only now, so the first barrier does not wait for
+  // them and they overlap the first scores.
+  {
+    const size_t ro = (size_t)row * D;
+#pragma unroll
+    for (int b = 0; b < kDB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 x = row_ok ? *reinterpret_cast<const float4 *>(O + ro + b * 32 + g * 8 + h * 4)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        oacc[b][4 * g + 0] = x.x;
+        oacc[b][4 * g + 1] = x.y;
+        oacc[b][4 * g + 2] = x.z;
+        oacc[b][4 * g + 3] = x.w;
+      }
+  }
   f32x16 s_cur[2];
   {
     scores(s_cur, lds_k0);   // tile 0 is never skipped
