@@ -444,8 +444,10 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       accumulate(pb, v_src);
       alpha = tile_max_update(s_nxt, rs, sl2, has_next, rescale);
       // Interleave: per score MFMA one LDS read and four vector instructions
-      // (exponentials of tile t), then per P V MFMA two LDS reads and two
-      // vector instructions (row maximum of tile t+1).
+      // (exponentials of tile t), then per P V MFMA two LDS reads and up to
+      // four vector instructions (the rest of the exponentials, then the row
+      // maximum of tile t+1).  The slots cover every vector instruction of
+      // the block, so none is left for a serial tail after the last MFMA.
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < 2 * kQK; ++i) {
@@ -457,7 +459,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       for (int i = 0; i < 4 * kDB; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
       }
     } else {
       const bool run_next = has_next && !skip_tile(t + 1);
@@ -530,8 +532,8 @@ hipError_t launch(const StepArgs &a, hipStream_t s) {
 // waste less work on the masked triangle and balance better.
 template <int D, bool kDiag>
 hipError_t launch_d(const StepArgs &a, hipStream_t s) {
-  if (kDiag) return launch<D, kDiag, 4>(a, s);
-  return launch<D, kDiag, 8>(a, s);
+  if constexpr (kDiag) return launch<D, kDiag, 4>(a, s);
+  else return launch<D, kDiag, 8>(a, s);
 }
 
 }  // namespace
