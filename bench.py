@@ -137,6 +137,7 @@ def main():
 
     import torch
     from ring_attention_block_amd import _lib
+    from ring_attention_block_amd.hip_events import Event
     from ring_attention_block_amd.ring import RingEmulator
 
     if not torch.cuda.is_available():
@@ -167,19 +168,24 @@ def main():
     o_out = torch.empty(st.o.shape, dtype=torch.float32, device=dev)
     lse_out = torch.empty(st.m.shape, dtype=torch.float32, device=dev)
 
-    def one_ring(timers=None):
+    def one_ring(timers=None, pool=None):
         emu.run(st, q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
-                step_timers=timers)
+                step_timers=timers, timer_events=pool)
         _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
 
     for _ in range(args.warmup):
         one_ring()
     torch.cuda.synchronize()
 
+    # Timing events for every launched step of the timed rings, created
+    # before the timed region.
+    launched = sum(_lib.step_case(rank, j, wl.blocks, wl.causal) != _lib.RA_CASE_SKIP
+                   for j in range(wl.blocks))
+    pool = iter([Event(timing=True) for _ in range(2 * launched * args.steps)])
     timers = []
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        one_ring(timers)
+        one_ring(timers, pool)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 

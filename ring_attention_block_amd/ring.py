@@ -50,13 +50,15 @@ class RingEmulator:
     def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
             rank: int, num_blocks: int, causal: bool, scale: float,
             order: Sequence[int] | None = None, init: bool = True,
-            step_timers: list | None = None) -> list:
+            step_timers: list | None = None, timer_events=None) -> list:
         """Fold the blocks of `order` (default: the ring order of `rank`) into st.
 
         kv_source(j) returns the resident (K_j, V_j) device tensors.
         step_timers, if given, receives (case, start_event, end_event) per
-        launched step, recorded on the compute stream around the launch.
-        Returns the causal case of each step.
+        launched step, recorded on the compute stream around the launch;
+        timer_events, if given, is an iterator of timing events created
+        beforehand (two per launched step), so that no event is created while
+        work is being enqueued.  Returns the causal case of each step.
         """
         order = ring_order(rank, num_blocks) if order is None else list(order)
         comp, copy = self.compute, self.copy
@@ -84,7 +86,10 @@ class RingEmulator:
                 self.ev_ready[cur_buf].wait(comp)
             case = _lib.step_case(rank, j, num_blocks, causal)
             if step_timers is not None and case != _lib.RA_CASE_SKIP:
-                e0, e1 = Event(timing=True), Event(timing=True)
+                if timer_events is not None:
+                    e0, e1 = next(timer_events), next(timer_events)
+                else:
+                    e0, e1 = Event(timing=True), Event(timing=True)
                 e0.record(comp)
                 _lib.step(st, q, cur[0], cur[1], rank, j, num_blocks, causal, scale, comp)
                 e1.record(comp)
