@@ -51,12 +51,13 @@ def full_step_flops(wl):
     return 4 * wl.head_dim * wl.heads * wl.rows * wl.rows
 
 
-def generate(wl, rank, threads=16):
-    """Seeded blocks of the workload (Q of the rank, every K and V), in parallel;
-    each block has its own seed, so threading does not change any value."""
+def generate(wl, rank, threads=16, q_blocks=None):
+    """Seeded blocks of the workload (Q of the rank's blocks, every K and V), in
+    parallel; each block has its own seed, so threading does not change any value."""
     import concurrent.futures as cf
-    jobs = [(synth.ROLE_Q, rank)] + [(r, j) for j in range(wl.blocks)
-                                     for r in (synth.ROLE_K, synth.ROLE_V)]
+    q_blocks = (rank,) if q_blocks is None else tuple(q_blocks)
+    jobs = [(synth.ROLE_Q, b) for b in q_blocks] + [(r, j) for j in range(wl.blocks)
+                                                    for r in (synth.ROLE_K, synth.ROLE_V)]
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         arrs = list(ex.map(lambda rj: synth.block(wl, *rj), jobs))
     return dict(zip(jobs, arrs))
@@ -126,6 +127,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--rank", type=int, default=None)
+    ap.add_argument("--partition", default="contiguous", choices=("contiguous", "zigzag"),
+                    help="contiguous: rank i holds block i; zigzag: the sequence in 2P pieces, "
+                         "rank i holds pieces i and 2P-1-i")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -138,7 +142,8 @@ def main():
     import torch
     from ring_attention_block_amd import _lib
     from ring_attention_block_amd.hip_events import Event
-    from ring_attention_block_amd.ring import RingEmulator
+    from ring_attention_block_amd.ring import (RingEmulator, ZigzagRing, zigzag_blocks,
+                                               zigzag_plan)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -149,29 +154,64 @@ def main():
     rank = args.rank if args.rank is not None else (
         DEFAULT_RANK if wl.name == DEFAULT_WORKLOAD else wl.ranks[-1])
     dev = "cuda"
+    compute = torch.cuda.Stream()
 
-    blocks = generate(wl, rank)
-
-    def to_dev(x):
-        if wl.dtype == "bf16":
+    def to_dev(x, w):
+        if w.dtype == "bf16":
             t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
         else:
             t = torch.from_numpy(x)
         return t.reshape(1, *x.shape).to(dev)
 
-    q = to_dev(blocks[(synth.ROLE_Q, rank)])
-    kv = {j: (to_dev(blocks[(synth.ROLE_K, j)]), to_dev(blocks[(synth.ROLE_V, j)]))
-          for j in range(wl.blocks)}
-    st = _lib.State(1, wl.heads, wl.rows, wl.head_dim, device=dev)
-    compute = torch.cuda.Stream()
-    emu = RingEmulator(q.shape, q.dtype, dev, compute_stream=compute)
-    o_out = torch.empty(st.o.shape, dtype=torch.float32, device=dev)
-    lse_out = torch.empty(st.m.shape, dtype=torch.float32, device=dev)
+    if args.partition == "contiguous":
+        step_wl = wl
+        blocks = generate(wl, rank)
+        q = to_dev(blocks[(synth.ROLE_Q, rank)], wl)
+        kv = {j: (to_dev(blocks[(synth.ROLE_K, j)], wl), to_dev(blocks[(synth.ROLE_V, j)], wl))
+              for j in range(wl.blocks)}
+        states = [_lib.State(1, wl.heads, wl.rows, wl.head_dim, device=dev)]
+        emu = RingEmulator(q.shape, q.dtype, dev, compute_stream=compute)
+        cases = [_lib.step_case(rank, j, wl.blocks, wl.causal) for j in range(wl.blocks)]
+        flops = ring_flops(wl, rank)
+        baseline_q = rank
+
+        def fold(timers, pool):
+            emu.run(states[0], q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
+                    step_timers=timers, timer_events=pool)
+    else:
+        # Zigzag: the sequence in 2P pieces of c/2 tokens; the rank holds
+        # pieces (rank, 2P-1-rank), and each visit is up to four piece products.
+        step_wl = synth.zigzag_workload(wl)
+        mine = zigzag_blocks(rank, wl.blocks)
+        blocks = generate(step_wl, rank, q_blocks=mine)
+        qs = [to_dev(blocks[(synth.ROLE_Q, b)], step_wl) for b in mine]
+        kv = {b: (to_dev(blocks[(synth.ROLE_K, b)], step_wl),
+                  to_dev(blocks[(synth.ROLE_V, b)], step_wl)) for b in range(step_wl.blocks)}
+
+        def source(j):
+            a, b = zigzag_blocks(j, wl.blocks)
+            return kv[a][0], kv[b][0], kv[a][1], kv[b][1]
+
+        states = [_lib.State(1, wl.heads, step_wl.rows, wl.head_dim, device=dev)
+                  for _ in range(2)]
+        zz = ZigzagRing(qs[0].shape, qs[0].dtype, dev, compute_stream=compute)
+        cases = [c for _, prods in zigzag_plan(rank, wl.blocks, wl.causal) for _, _, c in prods]
+        c2 = step_wl.rows
+        flops = 4 * wl.head_dim * wl.heads * (cases.count(_lib.RA_CASE_FULL) * c2 * c2 +
+                                              cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
+        baseline_q = mine[1]
+
+        def fold(timers, pool):
+            zz.run(states, qs, source, rank, wl.blocks, wl.causal, wl.scale,
+                   step_timers=timers, timer_events=pool)
+
+    outs = [(torch.empty(st.o.shape, dtype=torch.float32, device=dev),
+             torch.empty(st.m.shape, dtype=torch.float32, device=dev)) for st in states]
 
     def one_ring(timers=None, pool=None):
-        emu.run(st, q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
-                step_timers=timers, timer_events=pool)
-        _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
+        fold(timers, pool)
+        for st, (o_out, lse_out) in zip(states, outs):
+            _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
 
     for _ in range(args.warmup):
         one_ring()
@@ -179,8 +219,7 @@ def main():
 
     # Timing events for every launched step of the timed rings, created
     # before the timed region.
-    launched = sum(_lib.step_case(rank, j, wl.blocks, wl.causal) != _lib.RA_CASE_SKIP
-                   for j in range(wl.blocks))
+    launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
     pool = iter([Event(timing=True) for _ in range(2 * launched * args.steps)])
     timers = []
     t0 = time.perf_counter()
@@ -190,16 +229,15 @@ def main():
     elapsed = time.perf_counter() - t0
 
     ms = elapsed / args.steps * 1e3
-    flops = ring_flops(wl, rank)
     tflops = flops / (ms / 1e3) / 1e12
 
     full = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_FULL]
     diag = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_DIAG]
     if full:
-        dom_ms, dom_flops, dom = float(np.mean(full)), full_step_flops(wl), "ra_step full"
+        dom_ms, dom_flops, dom = float(np.mean(full)), full_step_flops(step_wl), "ra_step full"
     else:
         dom_ms = float(np.mean(diag))
-        dom_flops = 4 * wl.head_dim * wl.heads * (wl.rows * (wl.rows + 1) // 2)
+        dom_flops = 4 * wl.head_dim * wl.heads * (step_wl.rows * (step_wl.rows + 1) // 2)
         dom = "ra_step diagonal"
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
@@ -217,20 +255,22 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
-        "config": {"workload": wl.name, "rank": rank, "heads": wl.heads,
-                   "head_dim": wl.head_dim, "rows_per_block": wl.rows, "blocks": wl.blocks,
-                   "causal": wl.causal, "tokens": wl.tokens, "flop_per_step": flops,
+        "config": {"workload": wl.name, "rank": rank, "partition": args.partition,
+                   "heads": wl.heads, "head_dim": wl.head_dim, "rows_per_block": wl.rows,
+                   "blocks": wl.blocks, "causal": wl.causal, "tokens": wl.tokens,
+                   "flop_per_step": flops,
                    "pct_of_mfma_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "kernel": dom,
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(wl) if full else None,
+                     "traffic": (measured_traffic(wl) if full and args.partition == "contiguous"
+                                 else None),
                      "avg_launch_ms": round(dom_ms, 5),
                      "launches": len(full) if full else len(diag),
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, rank, blocks)
+        line["cpu_baseline"] = cpu_baseline(step_wl, baseline_q, blocks)
     print(json.dumps(line), flush=True)
 
 

@@ -9,11 +9,21 @@ step.  "Ring Attentionï¼šæŠŠè¶…é•¿åºåˆ—æ²¿è®¾å¤‡çŽ¯æµåŠ¨", section "åŒç¼“å†²æ
 the compute that reads it has finished, and B must not be read before its
 transfer has finished.
 
-Here the "receive" is a device-to-device copy (ra_stage_block) of block j from
-where it sits in HBM into the free buffer, on a side stream; HIP events enforce
-both hazards.  Blocks that the causal rule skips are still staged, because the
-ring forwards them.  Step 0 computes on the rank's first block where it lies
-(its own block, which a real rank already holds).
+Here the "receive" is a device-to-device copy (ra_stage_block) of the visiting
+rank's tensors from where they sit in HBM into the free buffer, on a side
+stream; HIP events enforce both hazards.  Blocks that the causal rule skips
+are still staged, because the ring forwards them.  Step 0 computes on the
+rank's own tensors where they lie (a real rank already holds them).
+
+Two partitions of the sequence over the P ranks:
+  * contiguous: rank i holds block i of P equal blocks (RingEmulator.run);
+  * zigzag ("Ring Attention Paper Breakdown ...", section 5, and
+    "Ring Attentionï¼š...", section "Causal Attention è®©çŽ¯ä¸å†å®Œå…¨å¯¹ç§°"): the
+    sequence is cut into 2P sub-blocks and rank i holds sub-blocks i and
+    2P-1-i, so under the causal mask every rank has the same work
+    (ZigzagRing).  Each visit is then up to four ra_step calls on sub-block
+    pairs; ra_step's causal case test on 2P sub-block indices already gives
+    the skip / diagonal / full case of each pair.
 """
 from __future__ import annotations
 
@@ -30,73 +40,69 @@ def ring_order(rank: int, blocks: int) -> list:
     return [(rank - s) % blocks for s in range(blocks)]
 
 
+def zigzag_blocks(rank: int, ranks: int) -> tuple:
+    """The two sub-blocks (of 2*ranks) that `rank` holds under the zigzag partition."""
+    return (rank, 2 * ranks - 1 - rank)
+
+
+def zigzag_plan(rank: int, ranks: int, causal: bool) -> list:
+    """Per ring step: (visiting rank j, [(a, b, case)]) for the products of the
+    rank's query sub-block a (0, 1) with the visiting key/value sub-block b
+    (0, 1); case is ra_step's causal case over 2*ranks sub-blocks (skipped
+    pairs are listed too)."""
+    mine = zigzag_blocks(rank, ranks)
+    plan = []
+    for j in ring_order(rank, ranks):
+        theirs = zigzag_blocks(j, ranks)
+        prods = [(a, b, _lib.step_case(mine[a], theirs[b], 2 * ranks, causal))
+                 for a in range(2) for b in range(2)]
+        plan.append((j, prods))
+    return plan
+
+
 class RingEmulator:
     """Reusable buffers, streams and events for one rank's ring.
 
-    shape: [batch, heads, rows, head_dim] of one key (or value) block.
+    shape: [batch, heads, rows, head_dim] of one staged tensor;
+    tensors_per_visit: tensors staged per visiting rank (K, V for the
+    contiguous partition; K and V of two sub-blocks for zigzag).
     """
 
-    def __init__(self, shape, dtype, device="cuda", compute_stream=None, copy_stream=None):
+    def __init__(self, shape, dtype, device="cuda", compute_stream=None, copy_stream=None,
+                 tensors_per_visit: int = 2):
         self.shape = tuple(shape)
         self.dtype = dtype
-        self.bufs = [(torch.empty(self.shape, dtype=dtype, device=device),
-                      torch.empty(self.shape, dtype=dtype, device=device)) for _ in range(2)]
+        self.bufs = [tuple(torch.empty(self.shape, dtype=dtype, device=device)
+                           for _ in range(tensors_per_visit)) for _ in range(2)]
         self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
         self.copy = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
         self.ev_ready = [Event(), Event()]
         self.ev_free = [Event(), Event()]
         self.ev_start = Event()
 
-    def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
-            rank: int, num_blocks: int, causal: bool, scale: float,
-            order: Sequence[int] | None = None, init: bool = True,
-            step_timers: list | None = None, timer_events=None) -> list:
-        """Fold the blocks of `order` (default: the ring order of `rank`) into st.
-
-        kv_source(j) returns the resident (K_j, V_j) device tensors.
-        step_timers, if given, receives (case, start_event, end_event) per
-        launched step, recorded on the compute stream around the launch;
-        timer_events, if given, is an iterator of timing events created
-        beforehand (two per launched step), so that no event is created while
-        work is being enqueued.  Returns the causal case of each step.
-        """
-        order = ring_order(rank, num_blocks) if order is None else list(order)
+    def visit(self, order: Sequence[int], source: Callable[[int], tuple],
+              fold: Callable[[int, int, tuple], None]) -> None:
+        """The staging protocol: for each step s, fold(s, j, tensors) enqueues
+        the compute on visiting rank j = order[s] on the compute stream while
+        the tensors of order[s+1] are staged into the free buffer."""
         comp, copy = self.compute, self.copy
-        if init:
-            _lib.state_init(st, comp)
         # Copies of this run start after everything already queued on the
         # compute stream (earlier runs may still read the buffers).
         self.ev_start.record(comp)
         self.ev_start.wait(copy)
-
-        cur = kv_source(order[0])
+        cur = source(order[0])
         cur_buf = None           # index of the buffer `cur` lives in (None: source)
         free_buf = 0
-        cases = []
         for s, j in enumerate(order):
             nxt_buf = None
             if s + 1 < len(order):
                 nxt_buf = free_buf
-                k_src, v_src = kv_source(order[s + 1])
-                kb, vb = self.bufs[nxt_buf]
-                _lib.stage_block(kb, k_src, copy)
-                _lib.stage_block(vb, v_src, copy)
+                for dst, src in zip(self.bufs[nxt_buf], source(order[s + 1])):
+                    _lib.stage_block(dst, src, copy)
                 self.ev_ready[nxt_buf].record(copy)
             if cur_buf is not None:
                 self.ev_ready[cur_buf].wait(comp)
-            case = _lib.step_case(rank, j, num_blocks, causal)
-            if step_timers is not None and case != _lib.RA_CASE_SKIP:
-                if timer_events is not None:
-                    e0, e1 = next(timer_events), next(timer_events)
-                else:
-                    e0, e1 = Event(timing=True), Event(timing=True)
-                e0.record(comp)
-                _lib.step(st, q, cur[0], cur[1], rank, j, num_blocks, causal, scale, comp)
-                e1.record(comp)
-                step_timers.append((case, e0, e1))
-            else:
-                _lib.step(st, q, cur[0], cur[1], rank, j, num_blocks, causal, scale, comp)
-            cases.append(case)
+            fold(s, j, cur)
             if cur_buf is not None:
                 self.ev_free[cur_buf].record(comp)
             if nxt_buf is not None:
@@ -108,4 +114,87 @@ class RingEmulator:
                 else:
                     free_buf = 1 - nxt_buf
                 cur, cur_buf = self.bufs[nxt_buf], nxt_buf
+
+    def step(self, st, q, k, v, i, j, num_blocks, causal, scale, case, step_timers=None,
+             timer_events=None) -> None:
+        """One ra_step on the compute stream, bracketed by timing events when
+        step_timers is given (see run)."""
+        comp = self.compute
+        if step_timers is not None and case != _lib.RA_CASE_SKIP:
+            if timer_events is not None:
+                e0, e1 = next(timer_events), next(timer_events)
+            else:
+                e0, e1 = Event(timing=True), Event(timing=True)
+            e0.record(comp)
+            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp)
+            e1.record(comp)
+            step_timers.append((case, e0, e1))
+        else:
+            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp)
+
+    def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
+            rank: int, num_blocks: int, causal: bool, scale: float,
+            order: Sequence[int] | None = None, init: bool = True,
+            step_timers: list | None = None, timer_events=None) -> list:
+        """Contiguous partition: fold the blocks of `order` (default: the ring
+        order of `rank`) into st.
+
+        kv_source(j) returns the resident (K_j, V_j) device tensors.
+        step_timers, if given, receives (case, start_event, end_event) per
+        launched step, recorded on the compute stream around the launch;
+        timer_events, if given, is an iterator of timing events created
+        beforehand (two per launched step), so that no event is created while
+        work is being enqueued.  Returns the causal case of each step.
+        """
+        order = ring_order(rank, num_blocks) if order is None else list(order)
+        if init:
+            _lib.state_init(st, self.compute)
+        cases = []
+
+        def fold(s, j, kv):
+            case = _lib.step_case(rank, j, num_blocks, causal)
+            self.step(st, q, kv[0], kv[1], rank, j, num_blocks, causal, scale, case,
+                      step_timers, timer_events)
+            cases.append(case)
+
+        self.visit(order, kv_source, fold)
         return cases
+
+
+class ZigzagRing:
+    """One rank's ring under the zigzag partition.
+
+    sub_shape: [batch, heads, rows, head_dim] of one sub-block (rows = c / 2
+    for c tokens per rank).  The rank's query and state are two sub-block
+    tensors each (sub-blocks zigzag_blocks(rank, P)); kv_source(j) returns
+    (K_a, K_b, V_a, V_b) of rank j's two sub-blocks zigzag_blocks(j, P).
+    """
+
+    def __init__(self, sub_shape, dtype, device="cuda", compute_stream=None, copy_stream=None):
+        self.emu = RingEmulator(sub_shape, dtype, device, compute_stream, copy_stream,
+                                tensors_per_visit=4)
+
+    @property
+    def compute(self):
+        return self.emu.compute
+
+    def run(self, states: Sequence[_lib.State], qs: Sequence[torch.Tensor],
+            kv_source: Callable[[int], tuple], rank: int, ranks: int, causal: bool,
+            scale: float, init: bool = True, step_timers: list | None = None,
+            timer_events=None) -> list:
+        """Fold every visiting rank's two sub-blocks into the two states.
+        Returns zigzag_plan(rank, ranks, causal)."""
+        plan = zigzag_plan(rank, ranks, causal)
+        if init:
+            for st in states:
+                _lib.state_init(st, self.compute)
+        mine = zigzag_blocks(rank, ranks)
+
+        def fold(s, j, kv):
+            theirs = zigzag_blocks(j, ranks)
+            for a, b, case in plan[s][1]:
+                self.emu.step(states[a], qs[a], kv[b], kv[2 + b], mine[a], theirs[b],
+                              2 * ranks, causal, scale, case, step_timers, timer_events)
+
+        self.emu.visit([j for j, _ in plan], kv_source, fold)
+        return plan

@@ -13,7 +13,7 @@ all of its blocks on the host at once and any block can be regenerated alone.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -59,6 +59,15 @@ WORKLOADS = {
                  (63,), note="checked on 256 sampled query rows"),
     ]
 }
+
+
+def zigzag_workload(wl: Workload) -> Workload:
+    """The same sequence cut into 2P sub-blocks of rows/2 tokens (the zigzag
+    partition: rank i holds sub-blocks i and 2P-1-i).  Sub-block b is drawn
+    from the seeded generator with block index b."""
+    if wl.rows % 2:
+        raise ValueError(f"{wl.name}: zigzag needs an even block length, got {wl.rows}")
+    return replace(wl, name=wl.name + "_zigzag", rows=wl.rows // 2, blocks=2 * wl.blocks)
 
 
 def normal_block(seed: int, role: int, block: int, heads: int, rows: int,

@@ -1,0 +1,106 @@
+"""GPU parity of the zigzag partition: ZigzagRing through the C ABI against
+the fp64 CPU oracle.
+
+Under the zigzag partition ("Ring Attention Paper Breakdown: Blockwise
+Distributed Transformers for Near-Infinite Context", section 5) rank i holds
+pieces i and 2P-1-i of a sequence cut into 2P pieces.  The oracle is the dense
+definition at those pieces' global positions against every key piece; inputs
+come from ring_attention_block_amd.synth, expected values from oracle/ only.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from ring_attention_block_amd import _lib, synth
+from ring_attention_block_amd.ring import ZigzagRing, zigzag_blocks
+
+from _helpers import assert_close, gen_blocks, oracle_rank, to_device, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    _lib.lib()
+
+
+def run_zigzag(sub, rank, ranks, causal, cache):
+    """Resident pieces of `sub` (the zigzag sub-block workload), one ring of
+    `rank`; returns the finalized (O, LSE) of the rank's two pieces."""
+    jobs = [(synth.ROLE_Q, b) for b in zigzag_blocks(rank, ranks)]
+    jobs += [(r, b) for b in range(2 * ranks) for r in (synth.ROLE_K, synth.ROLE_V)]
+    missing = [j for j in jobs if j not in cache]
+    cache.update(gen_blocks(sub, missing))
+    dev = {key: to_device(cache[key], sub) for key in jobs}
+    qs = [dev[(synth.ROLE_Q, b)] for b in zigzag_blocks(rank, ranks)]
+
+    def source(j):
+        a, b = zigzag_blocks(j, ranks)
+        return (dev[(synth.ROLE_K, a)], dev[(synth.ROLE_K, b)],
+                dev[(synth.ROLE_V, a)], dev[(synth.ROLE_V, b)])
+
+    states = [_lib.State(1, sub.heads, sub.rows, sub.head_dim) for _ in range(2)]
+    ring = ZigzagRing(qs[0].shape, qs[0].dtype)
+    ring.run(states, qs, source, rank, ranks, causal, sub.scale)
+    outs = [_lib.finalize(st, torch.float32, ring.compute) for st in states]
+    torch.cuda.synchronize()
+    return outs
+
+
+def check_rank(sub, rank, ranks, causal, cache, rows=None):
+    outs = run_zigzag(sub, rank, ranks, causal, cache)
+    to, tl = tol_for(sub)
+    for piece, (o, lse) in zip(zigzag_blocks(rank, ranks), outs):
+        want_o, want_lse = oracle_rank(sub, piece, range(2 * ranks), causal, row_sel=rows,
+                                       cache=cache)
+        got_o, got_lse = o[0].cpu().numpy(), lse[0].cpu().numpy()
+        if rows is not None:
+            got_o, got_lse = got_o[:, rows], got_lse[:, rows]
+        what = f"{sub.name} causal={causal} rank {rank} piece {piece}"
+        eo = assert_close(got_o, want_o, to, what + " O")
+        el = assert_close(got_lse, want_lse, tl, what + " LSE")
+        _say(f"  {what}: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+
+
+SMALL = [
+    # (heads, head_dim, rows per rank, ranks, dtype): pieces of rows/2, ragged tails
+    (2, 128, 400, 3, "bf16"),
+    (1, 64, 128, 4, "f32"),
+    (3, 64, 258, 2, "bf16"),
+    (2, 128, 1024, 4, "bf16"),
+]
+
+
+@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL)
+@pytest.mark.parametrize("causal", [True, False])
+def test_zigzag_every_rank(heads, d, rows, P, dtype, causal):
+    wl = synth.Workload(f"zz_{dtype}_h{heads}_d{d}_c{rows}_p{P}", 200 + rows + d, heads, d, rows,
+                        P, dtype, causal, tuple(range(P)))
+    sub = synth.zigzag_workload(wl)
+    cache = {}
+    for rank in range(P):
+        _say(f"{sub.name} causal={causal} rank={rank}")
+        check_rank(sub, rank, P, causal, cache)
+
+
+@pytest.mark.timeout(900)
+def test_zigzag_headline_shape_sampled_rows():
+    """The headline shape (32 heads, d = 128, 4096 tokens per rank, 8 ranks)
+    under the zigzag partition, ranks 0 and 7, on 64 sampled rows per piece."""
+    wl = synth.WORKLOADS["causal_bf16_h32_d128_c4096_p8"]
+    sub = synth.zigzag_workload(wl)
+    rows = synth.sample_rows(wl.seed, sub.rows, 64)
+    cache = {}
+    for rank in (0, 7):
+        _say(f"{sub.name} rank={rank}")
+        check_rank(sub, rank, wl.blocks, True, cache, rows=rows)
