@@ -29,6 +29,7 @@ from ring_attention_block_amd import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_FP32_VECTOR_TFLOPS = 157.3
+PEAK_HBM_BYTES = 8.0e12     # MI355X HBM3E, bytes/s
 HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "causal_bf16_h32_d128_c4096_p8"
 DEFAULT_RANK = 7
@@ -120,6 +121,60 @@ def cpu_baseline(wl, rank, blocks, target_s=15.0):
                       f"products, one thread for exp)"}
 
 
+def bench_decode(args, wl):
+    """Decode: args.decode_rows query rows (the tokens after the sequence)
+    against the workload's P blocks as key/value shards.  Memory-bound: the
+    figure of merit is the key/value bytes read per second."""
+    import torch
+    from ring_attention_block_amd.decode import ShardedDecode
+    from ring_attention_block_amd.hip_events import Event
+
+    rq, P, c = args.decode_rows, wl.blocks, wl.rows
+    blocks = generate(wl, P - 1)
+    dev = "cuda"
+
+    def to_dev(x):
+        t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if wl.dtype == "bf16" \
+            else torch.from_numpy(x)
+        return t.reshape(1, *x.shape).to(dev)
+
+    q = to_dev(synth.block(wl, synth.ROLE_Q, P, rows=rq))   # the tokens after the cache
+    kv = [(to_dev(blocks[(synth.ROLE_K, j)]), to_dev(blocks[(synth.ROLE_V, j)])) for j in range(P)]
+    compute = torch.cuda.Stream()
+    dec = ShardedDecode(q.shape, P, dev, compute_stream=compute)
+    o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        dec.run(q, kv, wl.scale, o_out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    e0, e1 = Event(timing=True), Event(timing=True)
+    t0 = time.perf_counter()
+    e0.record(compute)
+    for _ in range(args.steps):
+        dec.run(q, kv, wl.scale, o_out=o, lse_out=lse)
+    e1.record(compute)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    esize = 2 if wl.dtype == "bf16" else 4
+    kv_bytes = 2 * P * c * wl.heads * wl.head_dim * esize
+    flops = 4 * wl.head_dim * wl.heads * rq * P * c
+    line = {
+        "metric": "decode key/value read rate (GB/s)", "value": round(kv_bytes / (ms / 1e3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
+        "config": {"workload": wl.name, "mode": "decode", "query_rows": rq, "shards": P,
+                   "shard_rows": c, "heads": wl.heads, "head_dim": wl.head_dim,
+                   "kv_bytes": kv_bytes, "flop_per_step": flops,
+                   "tflops": round(flops / (ms / 1e3) / 1e12, 2),
+                   "pct_of_hbm_peak": round(100 * kv_bytes / (ms / 1e3) / PEAK_HBM_BYTES, 2)},
+        "compute_stream_ms": round(e0.elapsed_time(e1) / args.steps, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +185,10 @@ def main():
     ap.add_argument("--partition", default="contiguous", choices=("contiguous", "zigzag"),
                     help="contiguous: rank i holds block i; zigzag: the sequence in 2P pieces, "
                          "rank i holds pieces i and 2P-1-i")
+    ap.add_argument("--decode-rows", type=int, default=None,
+                    help="instead of the ring: decode this many query rows against the "
+                         "workload's P blocks as key/value shards (local fold per shard, "
+                         "tree of merges, finalize)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -151,6 +210,9 @@ def main():
     _lib.lib()   # fails loudly if libra.so is missing
 
     wl = synth.WORKLOADS[args.workload]
+    if args.decode_rows is not None:
+        bench_decode(args, wl)
+        return
     rank = args.rank if args.rank is not None else (
         DEFAULT_RANK if wl.name == DEFAULT_WORKLOAD else wl.ranks[-1])
     dev = "cuda"

@@ -19,9 +19,10 @@
  *   - Every pointer to tensor data is a device pointer (hipMalloc'd or torch
  *     CUDA memory) owned by the caller.  The library never allocates, frees or
  *     retains memory and never writes q, k or v.
- *   - Tensors are dense row-major: q, k, v and o are [batch, heads, rows,
- *     head_dim]; m, l and lse are [batch, heads, rows].  Every non-empty tensor
- *     pointer must be 16-byte aligned.
+ *   - Tensors are dense row-major: q and o are [batch, heads, rows,
+ *     head_dim], k and v [batch, heads, kv_rows, head_dim]; m, l and lse are
+ *     [batch, heads, rows].  Every non-empty tensor pointer must be 16-byte
+ *     aligned.
  *   - Every call is asynchronous and ordered on `stream` (0 = the null
  *     stream); no call synchronises.  Buffers must stay valid and unmodified
  *     until the stream has passed the call.
@@ -104,10 +105,14 @@ int32_t ra_step_case(int32_t q_block, int32_t kv_block, int32_t num_blocks, int3
  *   l' = exp(m - m') l + rowsum exp(S - m'),  O' = exp(m - m') O + exp(S - m') V_j.
  * On return of the kernel the state is again in the canonical form above
  * (m is the running maximum).
- *   q, k, v    [batch, heads, rows, head_dim] in in_dtype (RA_BF16 or RA_F32);
- *              q is the rank's block i, k and v are block j.
- *   kv_rows    rows of k and v; must equal st->rows (equal blocks), else
- *              RA_ERR_UNSUPPORTED.
+ *   q          [batch, heads, rows, head_dim] in in_dtype (RA_BF16 or RA_F32),
+ *              the rank's block i.
+ *   k, v       [batch, heads, kv_rows, head_dim] in in_dtype, block j.
+ *   kv_rows    rows of k and v, >= 0.  Under the causal mask it must equal
+ *              st->rows (the pages' equal blocks), else RA_ERR_UNSUPPORTED.
+ *              Without it any length is accepted: a short query block against
+ *              a key/value shard, as in decoding.  kv_rows == 0 folds nothing
+ *              (k and v may then be NULL).
  *   q_block, kv_block, num_blocks, causal   as in ra_step_case; global
  *              positions are q_block*rows + r and kv_block*rows + t.
  *   scale      score multiplier, finite and > 0 (1/sqrt(head_dim) normally).

@@ -133,8 +133,9 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
             raise ValueError(f"{name} must be contiguous")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
-    if q.shape != k.shape or k.shape != v.shape:
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if k.shape != v.shape or k.dim() != 4 or q.dim() != 4 or \
+            (q.shape[0], q.shape[1], q.shape[3]) != (k.shape[0], k.shape[1], k.shape[3]):
+        raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if tuple(q.shape) != st.shape:
         raise ValueError(f"q shape {tuple(q.shape)} does not match the state {st.shape}")
     _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),

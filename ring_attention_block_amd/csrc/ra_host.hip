@@ -111,17 +111,24 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
   if (in_dtype != RA_F32 && in_dtype != RA_BF16)
     return fail(RA_ERR_INVALID_ARG, "ra_step: in_dtype=%d is not RA_F32 or RA_BF16", (int)in_dtype);
   if (kv_rows < 0) return fail(RA_ERR_INVALID_ARG, "ra_step: kv_rows=%d is negative", kv_rows);
-  if (kv_rows != st->rows)
-    return fail(RA_ERR_UNSUPPORTED, "ra_step: kv_rows=%d differs from rows=%d (equal blocks only)",
+  if (kv_rows != st->rows && causal)
+    return fail(RA_ERR_UNSUPPORTED,
+                "ra_step: kv_rows=%d differs from rows=%d under the causal mask (equal blocks only)",
                 kv_rows, st->rows);
+  if ((int64_t)st->batch * st->heads * kv_rows > ((int64_t)1 << 40) / st->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "ra_step: key/value block of %d rows is too large", kv_rows);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(RA_ERR_INVALID_ARG, "ra_step: scale=%g must be finite and > 0", (double)scale);
   if (n > 0) {
-    if (!q || !k || !v) return fail(RA_ERR_INVALID_ARG, "ra_step: NULL q, k or v");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v))
-      return fail(RA_ERR_INVALID_ARG, "ra_step: q, k and v must be 16-byte aligned");
+    if (!q) return fail(RA_ERR_INVALID_ARG, "ra_step: NULL q");
+    if (!aligned16(q)) return fail(RA_ERR_INVALID_ARG, "ra_step: q must be 16-byte aligned");
+    if (kv_rows > 0) {
+      if (!k || !v) return fail(RA_ERR_INVALID_ARG, "ra_step: NULL k or v");
+      if (!aligned16(k) || !aligned16(v))
+        return fail(RA_ERR_INVALID_ARG, "ra_step: k and v must be 16-byte aligned");
+    }
   }
-  if (c == RA_CASE_SKIP || n == 0) return ok();  // future block / empty: nothing to fold
+  if (c == RA_CASE_SKIP || n == 0 || kv_rows == 0) return ok();  // nothing to fold
 
   ra::StepArgs a;
   a.q = q;
@@ -131,6 +138,7 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
   a.l = st->l;
   a.o = st->o;
   a.rows = st->rows;
+  a.kv_rows = kv_rows;
   a.bh = st->batch * st->heads;
   a.scale_log2 = scale * 1.442695040888963407f;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;

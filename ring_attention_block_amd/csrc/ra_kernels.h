@@ -12,7 +12,8 @@ namespace ra {
 struct StepArgs {
   const void *q, *k, *v;  // bf16 (uint16 storage) or fp32, per launcher
   float *m, *l, *o;       // state
-  int32_t rows;           // query rows == key rows of the block
+  int32_t rows;           // query rows of the block
+  int32_t kv_rows;        // key/value rows of the visiting block (== rows for a diagonal block)
   int32_t bh;             // batch * heads
   float scale_log2;       // score scale * log2(e): kernels work in base 2
 };

@@ -256,7 +256,8 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   __shared__ __attribute__((aligned(1024))) char lds_v0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_v1[T::kBytes];
 
-  const int rows = a.rows;
+  const int rows = a.rows;         // query rows
+  const int kv_rows = a.kv_rows;   // key/value rows (equal to rows on the diagonal)
   const int n_qt = (rows + kBM - 1) / kBM;
   // Workgroup -> (head, query tile).  Consecutive workgroup ids go to
   // different XCDs; when the head count allows, give each XCD a contiguous
@@ -285,14 +286,15 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   const bool row_ok = row < rows;
 
   const size_t base = (size_t)bh * rows * D;
+  const size_t kv_base = (size_t)bh * kv_rows * D;
   const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.q) + base;
   float *__restrict__ O = a.o + base;
-  const uint32_t blk_bytes = (uint32_t)rows * T::kRowBytes;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t *>(a.k) + base, blk_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t *>(a.v) + base, blk_bytes);
+  const uint32_t blk_bytes = (uint32_t)kv_rows * T::kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t *>(a.k) + kv_base, blk_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t *>(a.v) + kv_base, blk_bytes);
   const Stage<D, kW> so = stage_offsets<D, kW>(wave, lane);
 
-  const int kv_end = kDiag ? min(rows, qt * kBM + kBM) : rows;
+  const int kv_end = kDiag ? min(kv_rows, qt * kBM + kBM) : kv_rows;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   // Tile n uses K and V buffer n % 2.
 
@@ -301,8 +303,9 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // buffer holds finite keys/values of an earlier full tile there, which the
   // mask (keys) and the zero probabilities (values) already neutralise.
   const int last = n_tiles - 1;
-  if (last <= 1 && last * kBN + kBN > rows)
-    zero_tail<D, kW>((last & 1) ? lds_k1 : lds_k0, (last & 1) ? lds_v1 : lds_v0, rows - last * kBN, tid);
+  if (last <= 1 && last * kBN + kBN > kv_rows)
+    zero_tail<D, kW>((last & 1) ? lds_k1 : lds_k0, (last & 1) ? lds_v1 : lds_v0, kv_rows - last * kBN,
+                     tid);
   issue_copy<D, kW>(lds_k0, rk, so.k, 0, wave);
   issue_copy<D, kW>(lds_v0, rv, so.v, 0, wave);
   if (n_tiles > 1) issue_copy<D, kW>(lds_k1, rk, so.k, kBN, wave);
@@ -347,7 +350,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   }
 
   const float sl2 = a.scale_log2;
-  const int lim = kDiag ? min(row, rows - 1) : rows - 1;   // last key this row may see
+  const int lim = kDiag ? min(row, kv_rows - 1) : kv_rows - 1;   // last key this row may see
 
   // S^T = K Q^T for the tile in K buffer `kb`.
   auto scores = [&](f32x16 (&s)[2], const char *kb) {
@@ -382,7 +385,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // row of the wavefront) / needs the element mask.
   auto skip_tile = [&](int t) { return kDiag && t * kBN > q0w + 31; };
   auto mask_needed = [&](int t) {
-    return (kDiag && t * kBN + kBN - 1 > q0w) || (t * kBN + kBN > rows);
+    return (kDiag && t * kBN + kBN - 1 > q0w) || (t * kBN + kBN > kv_rows);
   };
 
   // Software pipeline, one tile ahead.  Iteration t issues the copies of
@@ -521,7 +524,7 @@ hipError_t launch(const StepArgs &a, hipStream_t s) {
   if constexpr (kDiag) {
     step_bf16_kernel<D, true, kW, true><<<grid, block, 0, s>>>(a);
   } else {
-    if (a.rows % kBN != 0) step_bf16_kernel<D, false, kW, true><<<grid, block, 0, s>>>(a);
+    if (a.kv_rows % kBN != 0) step_bf16_kernel<D, false, kW, true><<<grid, block, 0, s>>>(a);
     else step_bf16_kernel<D, false, kW, false><<<grid, block, 0, s>>>(a);
   }
   return hipGetLastError();

@@ -26,7 +26,8 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
   __shared__ float ks[kKeys][D];
   __shared__ float vs[kKeys][D];
 
-  const int rows = a.rows;
+  const int rows = a.rows;         // query rows
+  const int kv_rows = a.kv_rows;   // key/value rows (equal to rows on the diagonal)
   const int n_qt = (rows + kRows - 1) / kRows;
   const int bh = blockIdx.x / n_qt;
   const int qt = blockIdx.x % n_qt;
@@ -35,9 +36,10 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
   const int row = qt * kRows + r;
   const bool row_ok = row < rows;
   const size_t base = (size_t)bh * rows * D;
+  const size_t kv_base = (size_t)bh * kv_rows * D;
   const float *__restrict__ Q = static_cast<const float *>(a.q) + base;
-  const float *__restrict__ K = static_cast<const float *>(a.k) + base;
-  const float *__restrict__ V = static_cast<const float *>(a.v) + base;
+  const float *__restrict__ K = static_cast<const float *>(a.k) + kv_base;
+  const float *__restrict__ V = static_cast<const float *>(a.v) + kv_base;
   float *__restrict__ O = a.o + base;
   const size_t srow = (size_t)bh * rows + row;
 
@@ -50,12 +52,12 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
   float m2 = row_ok ? a.m[srow] * kLog2e : -INFINITY;  // base-2 running max
   float l = row_ok ? a.l[srow] : 0.f;
 
-  const int kv_end = kDiag ? min(rows, (qt + 1) * kRows) : rows;
+  const int kv_end = kDiag ? min(kv_rows, (qt + 1) * kRows) : kv_rows;
   for (int k0 = 0; k0 < kv_end; k0 += kKeys) {
     __syncthreads();
     for (int e = tid; e < kKeys * D; e += kThreads) {
       const int kr = e / D, kc = e % D;
-      const bool ok = k0 + kr < rows;
+      const bool ok = k0 + kr < kv_rows;
       ks[kr][kc] = ok ? K[(size_t)(k0 + kr) * D + kc] : 0.f;
       vs[kr][kc] = ok ? V[(size_t)(k0 + kr) * D + kc] : 0.f;
     }
@@ -71,7 +73,7 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
       acc += __shfl_xor(acc, 1);
       acc += __shfl_xor(acc, 2);
       const int key = k0 + j;
-      const bool ok = key < rows && (!kDiag || key <= row);
+      const bool ok = key < kv_rows && (!kDiag || key <= row);
       s[j] = ok ? acc : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }

@@ -1,0 +1,75 @@
+"""Decode / short query block against a sharded key/value cache, on one GPU.
+
+The pages' decoding pattern ("Ring Attention：把超长序列沿设备环流动", section
+"训练与推理的适用方式不同"): rather than passing key/value blocks around the ring
+for one new query, the short query block (the newest tokens) is broadcast to
+the ranks that hold the key/value shards; each rank folds it against its own
+shard into a partial softmax state, and a global online-softmax reduction
+combines the partial states.  The reduction is the merge of the aicassindra
+architecture article (section "The architecture: every piece explained"),
+whose identity is the empty state, so any tree of merges gives the same result
+up to rounding.
+
+The shards hold keys that every new token may see (the history before the
+block; a single new token's own key may be the last one), so the local folds
+run without the causal mask; that is what lets ra_step take a key/value block
+of another length than the query block.  Here the ranks are P streams of one GPU: the local folds run
+concurrently, and a binary tree of ra_lse_merge calls reduces the P states into
+state 0 on the compute stream, which then finalizes.
+"""
+from __future__ import annotations
+
+from typing import Sequence
+
+import torch
+
+from . import _lib
+from .hip_events import Event
+
+
+def merge_tree(shards: int) -> list:
+    """Levels of a binary reduction of `shards` states into state 0: each level
+    is a list of (dst, src) pairs whose merges are independent."""
+    levels, stride = [], 1
+    while stride < shards:
+        levels.append([(p, p + stride) for p in range(0, shards, 2 * stride) if p + stride < shards])
+        stride *= 2
+    return levels
+
+
+class ShardedDecode:
+    """Reusable states, streams and events for decoding against `shards` shards.
+
+    q_shape: [batch, heads, rows, head_dim] of the query block.
+    """
+
+    def __init__(self, q_shape, shards: int, device="cuda", compute_stream=None):
+        b, h, rows, d = q_shape
+        self.shards = shards
+        self.states = [_lib.State(b, h, rows, d, device=device) for _ in range(shards)]
+        self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+        self.streams = [torch.cuda.Stream(device=device) for _ in range(shards)]
+        self.ev_start = Event()
+        self.ev_done = [Event() for _ in range(shards)]
+
+    def run(self, q: torch.Tensor, kv: Sequence[tuple], scale: float, out_dtype=torch.float32,
+            o_out=None, lse_out=None):
+        """kv[p] = (K_p, V_p), [batch, heads, kv_rows_p, head_dim] each.  Returns
+        the finalized (O, LSE) of q against the concatenation of all shards."""
+        if len(kv) != self.shards:
+            raise ValueError(f"expected {self.shards} shards, got {len(kv)}")
+        # The local folds start after everything queued on the compute stream.
+        self.ev_start.record(self.compute)
+        for p, (k, v) in enumerate(kv):
+            s = self.streams[p]
+            self.ev_start.wait(s)
+            _lib.state_init(self.states[p], s)
+            _lib.step(self.states[p], q, k, v, 0, 0, 1, False, scale, s)
+            self.ev_done[p].record(s)
+        for p in range(self.shards):
+            self.ev_done[p].wait(self.compute)
+        for level in merge_tree(self.shards):
+            for dst, src in level:
+                _lib.lse_merge(self.states[dst], self.states[src], self.compute)
+        return _lib.finalize(self.states[0], out_dtype, self.compute, o_out=o_out,
+                             lse_out=lse_out)

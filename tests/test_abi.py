@@ -77,7 +77,11 @@ def test_step_rejects_before_enqueue(L):
     assert b"head_dim" in L.ra_last_error()
     assert _step(L, _state(d=0)) == _lib.RA_ERR_INVALID_ARG
     assert _step(L, _state(rows=-1)) == _lib.RA_ERR_INVALID_ARG
-    assert _step(L, st, kv_rows=64) == _lib.RA_ERR_UNSUPPORTED
+    assert _step(L, st, kv_rows=64) == _lib.RA_ERR_UNSUPPORTED   # causal needs equal blocks
+    assert b"causal" in L.ra_last_error()
+    assert _step(L, st, kv_rows=-1, causal=0) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, kv_rows=64, causal=0, k=0) == _lib.RA_ERR_INVALID_ARG
+    assert _step(L, st, kv_rows=64, causal=0, k=FAKE + 4) == _lib.RA_ERR_INVALID_ARG
     assert _step(L, st, i=2, P=2) == _lib.RA_ERR_INVALID_ARG
     assert _step(L, st, j=-1) == _lib.RA_ERR_INVALID_ARG
     assert _step(L, st, causal=3) == _lib.RA_ERR_INVALID_ARG
@@ -98,6 +102,8 @@ def test_skip_and_empty_enqueue_nothing(L):
     assert L.ra_last_error() == b""
     empty = _state(rows=0, m=0, l=0, o=0)
     assert _step(L, empty, q=0, k=0, v=0) == _lib.RA_OK
+    # an empty key/value block (non-causal) folds nothing; k and v may be NULL
+    assert _step(L, _state(), kv_rows=0, causal=0, k=0, v=0) == _lib.RA_OK
     assert L.ra_state_init(ctypes.byref(empty), None) == _lib.RA_OK
     assert L.ra_finalize(ctypes.byref(empty), None, 0, None, None) == _lib.RA_OK
     assert L.ra_lse_merge(ctypes.byref(empty), ctypes.byref(_state(rows=0, m=0, l=0, o=0)), None) == 0

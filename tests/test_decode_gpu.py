@@ -1,0 +1,100 @@
+"""GPU parity of decoding: a short query block against P key/value shards
+(ShardedDecode: local ra_step per shard with kv_rows != rows, tree of
+ra_lse_merge, finalize) against the fp64 oracle over the whole cache.
+
+Inputs come from ring_attention_block_amd.synth; expected values from oracle/.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import dense
+from ring_attention_block_amd import _lib, synth
+from ring_attention_block_amd.decode import ShardedDecode
+
+from _helpers import assert_close, oracle_values, to_device, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    _lib.lib()
+
+
+CASES = [
+    # (heads, head_dim, query rows, shard rows, shards, dtype)
+    (2, 128, 1, 4096, 8, "bf16"),
+    (4, 128, 16, 1000, 3, "bf16"),
+    (3, 64, 64, 200, 5, "bf16"),
+    (2, 64, 5, 129, 4, "f32"),
+    (1, 128, 300, 64, 2, "f32"),
+    (2, 128, 7, 333, 1, "bf16"),
+]
+
+
+@pytest.mark.parametrize("heads,d,rq,c,P,dtype", CASES)
+def test_decode_against_sharded_cache(heads, d, rq, c, P, dtype):
+    # Shards are blocks 0..P-1 of a workload with c rows per block; the query
+    # block is rq rows drawn as Q block P (the tokens after the cache).
+    wl = synth.Workload(f"dec_{dtype}_h{heads}_d{d}_q{rq}_c{c}_p{P}", 300 + rq + c, heads, d, c,
+                        P + 1, dtype, False, (P,))
+    _say(wl.name)
+    qh = synth.block(wl, synth.ROLE_Q, P, rows=rq)
+    assert qh.shape == (heads, rq, d)
+    kh = [synth.block(wl, synth.ROLE_K, j) for j in range(P)]
+    vh = [synth.block(wl, synth.ROLE_V, j) for j in range(P)]
+    q = to_device(qh, wl)
+    kv = [(to_device(k, wl), to_device(v, wl)) for k, v in zip(kh, vh)]
+    dec = ShardedDecode(q.shape, P)
+    o, lse = dec.run(q, kv, wl.scale)
+    torch.cuda.synchronize()
+    to, tl = tol_for(wl)
+    kp = np.arange(P * c)
+    qp = np.full(rq, P * c)
+    for hh in range(heads):
+        want_o, want_lse = dense.attention(
+            oracle_values(qh[hh:hh + 1], wl),
+            np.concatenate([oracle_values(k[hh:hh + 1], wl) for k in kh], axis=1),
+            np.concatenate([oracle_values(v[hh:hh + 1], wl) for v in vh], axis=1),
+            qp, kp, False, wl.scale)
+        eo = assert_close(o[0, hh].cpu().numpy(), want_o[0], to, f"head {hh} O")
+        el = assert_close(lse[0, hh].cpu().numpy(), want_lse[0], tl, f"head {hh} LSE")
+    _say(f"  max|dO|={eo:.2e} max|dLSE|={el:.2e} (last head)")
+
+
+def test_unequal_block_step_matches_merge_of_halves():
+    """One non-causal ra_step over a 2c-row key/value block agrees with the
+    merge of two c-row steps; and a zero-row block leaves the state bit-identical."""
+    wl = synth.Workload("dec_split", 77, 2, 128, 256, 3, "bf16", False, (2,))
+    q = to_device(synth.block(wl, synth.ROLE_Q, 2, rows=40), wl)
+    k = [to_device(synth.block(wl, synth.ROLE_K, j), wl) for j in range(2)]
+    v = [to_device(synth.block(wl, synth.ROLE_V, j), wl) for j in range(2)]
+    st = _lib.State(1, 2, 40, 128)
+    _lib.state_init(st)
+    _lib.step(st, q, torch.cat(k, 2).contiguous(), torch.cat(v, 2).contiguous(), 0, 0, 1, False,
+              wl.scale)
+    before = [t.clone() for t in (st.m, st.l, st.o)]
+    empty = torch.empty(1, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
+    _lib.step(st, q, empty, empty, 0, 0, 1, False, wl.scale)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, (st.m, st.l, st.o)))
+    o1, lse1 = _lib.finalize(st)
+    dec = ShardedDecode(q.shape, 2)
+    o2, lse2 = dec.run(q, list(zip(k, v)), wl.scale)
+    torch.cuda.synchronize()
+    # Both round P to bf16 (2^-9 relative per term), relative to different
+    # reference maxima, so they agree to that rounding level, well inside the
+    # oracle tolerance each of them meets.
+    assert_close(o1.cpu().numpy(), o2.cpu().numpy(), 2e-3, "O whole vs merged halves")
+    assert_close(lse1.cpu().numpy(), lse2.cpu().numpy(), 2e-3, "LSE whole vs merged halves")
