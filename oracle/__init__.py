@@ -13,7 +13,11 @@ Contents
                 dense oracle (block order, merge, skip) and to check the
                 intermediate values of the worked example.
   brute      -- 50-digit decimal brute force for tiny inputs.
+  backward   -- the fp64 gradients (dQ, dK, dV) of the dense forward, and the
+                per-key-block contribution with probabilities recomputed from
+                the saved log-sum-exp (what a ring rank accumulates).
 
-Every function here is pinned by tests/test_oracle.py against values fixed by
-the pages or by mathematics; none is "parity unpinned".
+Every function here is pinned by tests/test_oracle.py and
+tests/test_oracle_backward.py against values fixed by the pages or by
+mathematics; none is "parity unpinned".
 """
