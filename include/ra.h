@@ -161,6 +161,50 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
  */
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream);
 
+/*
+ * Backward, per-row term ("Ring Attention：...", section "Backward 需要让梯度也
+ * 沿环传播": gradients of every block interaction, probabilities recomputed
+ * from the saved log-sum-exp):  delta[row] = sum_x dout[row][x] * o[row][x],
+ * the D of dS = P (dP - D), computed once per rank before its backward ring.
+ *   o       [batch, heads, rows, head_dim] the forward output (ra_finalize's
+ *           o_out, normalised) in o_dtype (RA_F32 or RA_BF16)
+ *   dout    [batch, heads, rows, head_dim] gradient of the loss with respect
+ *           to that output, in do_dtype
+ *   delta   [batch, heads, rows] fp32, written
+ * head_dim 64 or 128 (else RA_ERR_UNSUPPORTED); checks and errors as for
+ * ra_step.
+ */
+ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
+                         const void *o, ra_dtype o_dtype, const void *dout, ra_dtype do_dtype,
+                         float *delta, hipStream_t stream);
+
+/*
+ * Backward of one ring step: the contribution of visiting block j to the
+ * gradients of query block i (same section; the query owner accumulates dq,
+ * the dk and dv of block j accumulate while it travels the ring and return to
+ * its owner):
+ *   P = exp(scale * q k^T - lse)   (masked per ra_step_case; a row with
+ *                                   lse = -inf contributes nothing)
+ *   dP = dout v^T,  dS = P * (dP - delta)
+ *   dq += scale * dS k,   dk += scale * dS^T q,   dv += P^T dout
+ *   q, dout   [batch, heads, rows, head_dim] in in_dtype, block i
+ *   lse       [batch, heads, rows] fp32, natural log (ra_finalize's lse_out)
+ *   delta     [batch, heads, rows] fp32 (ra_bwd_prepare)
+ *   k, v      [batch, heads, rows, head_dim] in in_dtype, block j (equal blocks)
+ *   dq        [batch, heads, rows, head_dim] fp32, accumulated (block i)
+ *   dk, dv    [batch, heads, rows, head_dim] fp32, accumulated (block j)
+ *   q_block, kv_block, num_blocks, causal, scale   as in ra_step.
+ * The caller zeroes the accumulators before a ring.  A skipped block returns
+ * RA_OK and enqueues nothing.  dk and dv are updated with fp32 atomics where
+ * several query tiles add to the same keys, so their low bits may differ
+ * between runs; dq is written by one workgroup per row.
+ */
+ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim, const void *q,
+                      const void *dout, const float *lse, const float *delta, const void *k,
+                      const void *v, ra_dtype in_dtype, float *dq, float *dk, float *dv,
+                      int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
+                      float scale, hipStream_t stream);
+
 /* Static string naming a status code. */
 const char *ra_status_string(ra_status s);
 

@@ -20,7 +20,7 @@ RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
 
 # Every symbol include/ra.h declares.
 EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_lse_merge", "ra_finalize",
-           "ra_stage_block", "ra_status_string", "ra_last_error")
+           "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_status_string", "ra_last_error")
 
 
 class RaState(ctypes.Structure):
@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
             "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
             "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
+            "ra_bwd_prepare": (ctypes.c_int, [i32, i32, i32, i32, vp, ctypes.c_int, vp, ctypes.c_int,
+                                              vp, vp]),
+            "ra_bwd_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_int,
+                                           vp, vp, vp, i32, i32, i32, i32, f32, vp]),
             "ra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "ra_last_error": (ctypes.c_char_p, []),
         }
@@ -167,3 +171,40 @@ def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
         raise ValueError("stage_block: sizes differ")
     _check(lib().ra_stage_block(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
                                 _stream(stream)))
+
+
+def bwd_prepare(o, dout, delta=None, stream=None):
+    """delta = rowsum(dout * o) [B,H,rows] fp32 (o: the forward output)."""
+    for name, t in (("o", o), ("dout", dout)):
+        if not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous [B,H,rows,d] tensor")
+    if o.shape != dout.shape:
+        raise ValueError(f"o {tuple(o.shape)} and dout {tuple(dout.shape)} differ")
+    b, h, r, d = o.shape
+    if delta is None:
+        delta = torch.empty((b, h, r), dtype=torch.float32, device=o.device)
+    _check(lib().ra_bwd_prepare(b, h, r, d, _ptr(o), _dtype_code(o), _ptr(dout), _dtype_code(dout),
+                                _ptr(delta), _stream(stream)))
+    return delta
+
+
+def bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_block: int, kv_block: int,
+             num_blocks: int, causal: bool, scale: float, stream=None) -> int:
+    """Add block kv_block's backward contribution: dq += ..., dk += ..., dv += ...
+    Returns the causal case."""
+    tensors = (("q", q), ("dout", dout), ("k", k), ("v", v), ("dq", dq), ("dk", dk), ("dv", dv))
+    for name, t in tensors:
+        if not t.is_contiguous() or tuple(t.shape) != tuple(q.shape):
+            raise ValueError(f"{name} must be contiguous with the shape of q {tuple(q.shape)}")
+    if not (q.dtype == dout.dtype == k.dtype == v.dtype):
+        raise TypeError("q, dout, k and v must share one dtype")
+    if not (dq.dtype == dk.dtype == dv.dtype == torch.float32):
+        raise TypeError("dq, dk and dv must be float32 accumulators")
+    b, h, r, d = q.shape
+    for name, t in (("lse", lse), ("delta", delta)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (b, h, r) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [B,H,rows] tensor")
+    _check(lib().ra_bwd_step(b, h, r, d, _ptr(q), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(k),
+                             _ptr(v), _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), q_block,
+                             kv_block, num_blocks, int(causal), float(scale), _stream(stream)))
+    return step_case(q_block, kv_block, num_blocks, causal)

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libra.so")
 ARCH = "gfx950"
 
-SOURCES = ["ra_host.hip", "ra_state.hip", "ra_stage.hip", "ra_step_f32.hip", "ra_step_bf16.hip"]
+SOURCES = ["ra_host.hip", "ra_state.hip", "ra_stage.hip", "ra_step_f32.hip", "ra_step_bf16.hip",
+           "ra_bwd.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

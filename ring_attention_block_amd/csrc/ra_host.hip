@@ -31,20 +31,31 @@ ra_status ok() {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Rows of a state (batch * heads * rows) or -1 on a malformed shape.
+// Shape rules shared by every entry point: rows >= 0, head_dim 64 or 128, and
+// the row count bounded so that element offsets fit comfortably in 64 bits.
+ra_status check_shape(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
+                      const char *name, int64_t *n_rows) {
+  if (batch < 0 || heads < 0 || rows < 0)
+    return fail(RA_ERR_INVALID_ARG, "%s: negative shape (batch=%d heads=%d rows=%d)", name,
+                batch, heads, rows);
+  if (head_dim <= 0)
+    return fail(RA_ERR_INVALID_ARG, "%s: head_dim=%d must be positive", name, head_dim);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(RA_ERR_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", name, head_dim);
+  const int64_t bh = (int64_t)batch * heads;
+  if (bh > INT32_MAX) return fail(RA_ERR_INVALID_ARG, "%s: batch*heads exceeds 2^31-1", name);
+  const int64_t n = bh * rows;
+  if (n > ((int64_t)1 << 40) / head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: %lld rows is too large", name, (long long)n);
+  *n_rows = n;
+  return RA_OK;
+}
+
 ra_status check_state(const ra_state *st, const char *name, int64_t *n_rows) {
   if (!st) return fail(RA_ERR_INVALID_ARG, "%s: state pointer is NULL", name);
-  if (st->batch < 0 || st->heads < 0 || st->rows < 0)
-    return fail(RA_ERR_INVALID_ARG, "%s: negative shape (batch=%d heads=%d rows=%d)", name,
-                st->batch, st->heads, st->rows);
-  if (st->head_dim <= 0)
-    return fail(RA_ERR_INVALID_ARG, "%s: head_dim=%d must be positive", name, st->head_dim);
-  if (st->head_dim != 64 && st->head_dim != 128)
-    return fail(RA_ERR_UNSUPPORTED, "%s: head_dim=%d (supported: 64, 128)", name, st->head_dim);
-  const int64_t bh = (int64_t)st->batch * st->heads;
-  if (bh > INT32_MAX) return fail(RA_ERR_INVALID_ARG, "%s: batch*heads exceeds 2^31-1", name);
-  const int64_t n = bh * st->rows;
-  if (n > ((int64_t)1 << 40) / st->head_dim)
-    return fail(RA_ERR_INVALID_ARG, "%s: state of %lld rows is too large", name, (long long)n);
+  int64_t n = 0;
+  const ra_status s = check_shape(st->batch, st->heads, st->rows, st->head_dim, name, &n);
+  if (s != RA_OK) return s;
   if (n > 0) {
     if (!st->m || !st->l || !st->o)
       return fail(RA_ERR_INVALID_ARG, "%s: NULL m, l or o with %lld rows", name, (long long)n);
@@ -181,6 +192,66 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
   return hip_status(ra::launch_finalize(st->m, st->l, st->o, o_out, out_dtype == RA_BF16,
                                         lse_out, n, st->head_dim, stream),
                     "ra_finalize launch");
+}
+
+ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
+                         const void *o, ra_dtype o_dtype, const void *dout, ra_dtype do_dtype,
+                         float *delta, hipStream_t stream) {
+  int64_t n = 0;
+  ra_status s = check_shape(batch, heads, rows, head_dim, "ra_bwd_prepare", &n);
+  if (s != RA_OK) return s;
+  if ((o_dtype != RA_F32 && o_dtype != RA_BF16) || (do_dtype != RA_F32 && do_dtype != RA_BF16))
+    return fail(RA_ERR_INVALID_ARG, "ra_bwd_prepare: o_dtype and do_dtype must be RA_F32 or RA_BF16");
+  if (n == 0) return ok();
+  if (!o || !dout || !delta || !aligned16(o) || !aligned16(dout) || !aligned16(delta))
+    return fail(RA_ERR_INVALID_ARG,
+                "ra_bwd_prepare: o, dout and delta must be non-NULL and 16-byte aligned");
+  (void)hipGetLastError();
+  return hip_status(ra::launch_bwd_prepare(o, o_dtype == RA_BF16, dout, do_dtype == RA_BF16, delta,
+                                           n, head_dim, stream),
+                    "ra_bwd_prepare launch");
+}
+
+ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim, const void *q,
+                      const void *dout, const float *lse, const float *delta, const void *k,
+                      const void *v, ra_dtype in_dtype, float *dq, float *dk, float *dv,
+                      int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
+                      float scale, hipStream_t stream) {
+  int64_t n = 0;
+  ra_status s = check_shape(batch, heads, rows, head_dim, "ra_bwd_step", &n);
+  if (s != RA_OK) return s;
+  const int32_t c = ra_step_case(q_block, kv_block, num_blocks, causal);
+  if (c < 0) return (ra_status)c;
+  if (in_dtype != RA_F32 && in_dtype != RA_BF16)
+    return fail(RA_ERR_INVALID_ARG, "ra_bwd_step: in_dtype=%d is not RA_F32 or RA_BF16", (int)in_dtype);
+  if (!(scale > 0.f) || !isfinite(scale))
+    return fail(RA_ERR_INVALID_ARG, "ra_bwd_step: scale=%g must be finite and > 0", (double)scale);
+  if (n > 0) {
+    const void *ptrs[] = {q, dout, lse, delta, k, v, dq, dk, dv};
+    for (const void *p : ptrs)
+      if (!p || !aligned16(p))
+        return fail(RA_ERR_INVALID_ARG,
+                    "ra_bwd_step: q, dout, lse, delta, k, v, dq, dk, dv must be non-NULL and 16-byte aligned");
+  }
+  if (c == RA_CASE_SKIP || n == 0) return ok();
+  ra::BwdArgs a;
+  a.q = q;
+  a.dout = dout;
+  a.k = k;
+  a.v = v;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.rows = rows;
+  a.bh = batch * heads;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.442695040888963407f;
+  const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
+  (void)hipGetLastError();
+  return hip_status(ra::launch_bwd_step_simple(a, head_dim, in_dtype == RA_BF16, sc, stream),
+                    "ra_bwd_step launch");
 }
 
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream) {

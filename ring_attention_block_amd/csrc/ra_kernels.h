@@ -20,6 +20,19 @@ struct StepArgs {
 
 enum class StepCase : int { Diag = 1, Full = 2 };
 
+// Arguments of one backward-step launch.  Tensors are [bh, rows, D]; the query
+// side (q, dout, lse, delta, dq) belongs to block i, the key side (k, v, dk,
+// dv) to block j.  dq, dk, dv are fp32 accumulators.
+struct BwdArgs {
+  const void *q, *dout, *k, *v;  // bf16 (uint16 storage) or fp32, per launcher
+  const float *lse, *delta;      // per query row: natural-log LSE, rowsum(dO * O)
+  float *dq, *dk, *dv;
+  int32_t rows;
+  int32_t bh;
+  float scale;                   // score scale
+  float scale_log2;              // scale * log2(e)
+};
+
 hipError_t launch_state_init(float *m, float *l, float *o, int64_t n_rows, int d,
                              hipStream_t s);
 hipError_t launch_state_merge(float *dm, float *dl, float *dO, const float *sm, const float *sl,
@@ -30,5 +43,8 @@ hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s)
 hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s);
 // bytes a multiple of 16, both pointers 16-byte aligned, no overlap.
 hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_bwd_prepare(const void *o, bool o_bf16, const void *dout, bool do_bf16,
+                              float *delta, int64_t n_rows, int d, hipStream_t s);
+hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s);
 
 }  // namespace ra

@@ -65,15 +65,18 @@ class RingEmulator:
 
     shape: [batch, heads, rows, head_dim] of one staged tensor;
     tensors_per_visit: tensors staged per visiting rank (K, V for the
-    contiguous partition; K and V of two sub-blocks for zigzag).
+    contiguous partition; K and V of two sub-blocks for zigzag);
+    extra_specs: (shape, dtype) of further tensors staged with them (the
+    travelling dK, dV accumulators of the backward).
     """
 
     def __init__(self, shape, dtype, device="cuda", compute_stream=None, copy_stream=None,
-                 tensors_per_visit: int = 2):
+                 tensors_per_visit: int = 2, extra_specs=()):
         self.shape = tuple(shape)
         self.dtype = dtype
-        self.bufs = [tuple(torch.empty(self.shape, dtype=dtype, device=device)
-                           for _ in range(tensors_per_visit)) for _ in range(2)]
+        specs = [(self.shape, dtype)] * tensors_per_visit + [(tuple(sh), dt) for sh, dt in extra_specs]
+        self.bufs = [tuple(torch.empty(sh, dtype=dt, device=device) for sh, dt in specs)
+                     for _ in range(2)]
         self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
         self.copy = copy_stream if copy_stream is not None else torch.cuda.Stream(device=device)
         self.ev_ready = [Event(), Event()]
@@ -81,10 +84,15 @@ class RingEmulator:
         self.ev_start = Event()
 
     def visit(self, order: Sequence[int], source: Callable[[int], tuple],
-              fold: Callable[[int, int, tuple], None]) -> None:
+              fold: Callable[[int, int, tuple], None], drain=None) -> None:
         """The staging protocol: for each step s, fold(s, j, tensors) enqueues
         the compute on visiting rank j = order[s] on the compute stream while
-        the tensors of order[s+1] are staged into the free buffer."""
+        the tensors of order[s+1] are staged into the free buffer.
+
+        drain(j, tensors, stream), if given, is enqueued on the copy stream
+        once the compute on a staged buffer has finished and before the buffer
+        is refilled: the send of what the step updated (the backward's dK, dV)
+        to the next rank.  The compute stream waits for the last drain."""
         comp, copy = self.compute, self.copy
         # Copies of this run start after everything already queued on the
         # compute stream (earlier runs may still read the buffers).
@@ -105,15 +113,17 @@ class RingEmulator:
             fold(s, j, cur)
             if cur_buf is not None:
                 self.ev_free[cur_buf].record(comp)
+                self.ev_free[cur_buf].wait(copy)
+                if drain is not None:
+                    drain(j, cur, copy)
             if nxt_buf is not None:
                 # The buffer just computed on becomes the next receive target;
-                # the copy stream waits for its free event before refilling it.
-                if cur_buf is not None:
-                    free_buf = cur_buf
-                    self.ev_free[cur_buf].wait(copy)
-                else:
-                    free_buf = 1 - nxt_buf
+                # the copy stream has waited for its free event before refilling it.
+                free_buf = cur_buf if cur_buf is not None else 1 - nxt_buf
                 cur, cur_buf = self.bufs[nxt_buf], nxt_buf
+        if drain is not None:
+            self.ev_start.record(copy)
+            self.ev_start.wait(comp)
 
     def step(self, st, q, k, v, i, j, num_blocks, causal, scale, case, step_timers=None,
              timer_events=None) -> None:
@@ -158,6 +168,44 @@ class RingEmulator:
             cases.append(case)
 
         self.visit(order, kv_source, fold)
+        return cases
+
+
+    def run_backward(self, q, dout, lse, delta, dq, source: Callable[[int], tuple],
+                     rank: int, num_blocks: int, causal: bool, scale: float,
+                     step_timers: list | None = None, timer_events=None) -> list:
+        """Backward ring of `rank` ("Ring Attention：...", section "Backward
+        需要让梯度也沿环传播"): dq (fp32, zeroed by the caller) accumulates the
+        contributions of every visiting block; source(j) returns block j's
+        resident (K_j, V_j, dK_j, dV_j), of which the fp32 dK_j, dV_j travel
+        with the block: they are staged in with K_j, V_j, the step adds this
+        rank's contribution, and they are sent on (copied back to the resident
+        tensors) after the step.  Needs extra_specs for dK, dV at construction.
+        Returns the causal case of each step."""
+        order = ring_order(rank, num_blocks)
+        cases = []
+
+        def fold(s, j, t):
+            case = _lib.step_case(rank, j, num_blocks, causal)
+            comp = self.compute
+            timed = step_timers is not None and case != _lib.RA_CASE_SKIP
+            if timed:
+                e0 = next(timer_events) if timer_events is not None else Event(timing=True)
+                e1 = next(timer_events) if timer_events is not None else Event(timing=True)
+                e0.record(comp)
+            _lib.bwd_step(q, dout, lse, delta, t[0], t[1], dq, t[2], t[3], rank, j, num_blocks,
+                          causal, scale, comp)
+            if timed:
+                e1.record(comp)
+                step_timers.append((case, e0, e1))
+            cases.append(case)
+
+        def drain(j, t, stream):
+            dk, dv = source(j)[2:4]
+            _lib.stage_block(dk, t[2], stream)
+            _lib.stage_block(dv, t[3], stream)
+
+        self.visit(order, source, fold, drain)
         return cases
 
 

@@ -18,6 +18,7 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 ROLE_Q, ROLE_K, ROLE_V = 0, 1, 2
+ROLE_DO = 3   # gradient of the loss with respect to the output (backward inputs)
 
 
 @dataclass(frozen=True)

@@ -125,3 +125,39 @@ def test_merge_finalize_stage_reject(L):
     assert L.ra_stage_block(FAKE, FAKE + 4096, 24, None) == _lib.RA_ERR_INVALID_ARG
     assert b"aligned" in L.ra_last_error()
     assert L.ra_state_init(None, None) == _lib.RA_ERR_INVALID_ARG
+
+
+def _bwd(L, q=FAKE, dout=FAKE, lse=FAKE, delta=FAKE, k=FAKE, v=FAKE, dtype=_lib.RA_BF16,
+         dq=FAKE, dk=FAKE, dv=FAKE, i=1, j=0, P=2, causal=1, scale=0.125, rows=128, d=128):
+    return L.ra_bwd_step(1, 2, rows, d, q, dout, lse, delta, k, v, dtype, dq, dk, dv, i, j, P,
+                         causal, scale, None)
+
+
+def test_bwd_rejects_before_enqueue(L):
+    assert _bwd(L, d=96) == _lib.RA_ERR_UNSUPPORTED
+    assert b"ra_bwd_step" in L.ra_last_error() and b"head_dim" in L.ra_last_error()
+    assert _bwd(L, rows=-1) == _lib.RA_ERR_INVALID_ARG
+    assert _bwd(L, i=2, P=2) == _lib.RA_ERR_INVALID_ARG
+    assert _bwd(L, causal=2) == _lib.RA_ERR_INVALID_ARG
+    assert _bwd(L, dtype=9) == _lib.RA_ERR_INVALID_ARG
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        assert _bwd(L, scale=bad) == _lib.RA_ERR_INVALID_ARG
+    for name in ("q", "dout", "lse", "delta", "k", "v", "dq", "dk", "dv"):
+        assert _bwd(L, **{name: 0}) == _lib.RA_ERR_INVALID_ARG, name
+        assert _bwd(L, **{name: FAKE + 4}) == _lib.RA_ERR_INVALID_ARG, name
+        assert b"aligned" in L.ra_last_error()
+    # a causal future block and an empty block enqueue nothing
+    assert _bwd(L, i=0, j=1) == _lib.RA_OK
+    assert _bwd(L, rows=0, q=0, dout=0, lse=0, delta=0, k=0, v=0, dq=0, dk=0, dv=0) == _lib.RA_OK
+
+    prep = lambda **kw: L.ra_bwd_prepare(1, 2, kw.get("rows", 128), kw.get("d", 128),
+                                         kw.get("o", FAKE), kw.get("ot", _lib.RA_F32),
+                                         kw.get("dout", FAKE), kw.get("dt", _lib.RA_BF16),
+                                         kw.get("delta", FAKE), None)
+    assert prep(d=32) == _lib.RA_ERR_UNSUPPORTED
+    assert prep(ot=4) == _lib.RA_ERR_INVALID_ARG
+    assert prep(dt=4) == _lib.RA_ERR_INVALID_ARG
+    for name in ("o", "dout", "delta"):
+        assert prep(**{name: 0}) == _lib.RA_ERR_INVALID_ARG, name
+        assert prep(**{name: FAKE + 8}) == _lib.RA_ERR_INVALID_ARG, name
+    assert prep(rows=0, o=0, dout=0, delta=0) == _lib.RA_OK

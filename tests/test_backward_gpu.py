@@ -1,0 +1,151 @@
+"""GPU parity of the backward ring step (ra_bwd_prepare, ra_bwd_step and the
+backward ring of RingEmulator) against the fp64 backward oracle.
+
+"Ring Attention：把超长序列沿设备环流动", section "Backward 需要让梯度也沿环传播":
+the query owner accumulates dQ, the dK and dV of a key/value block accumulate
+while it travels the ring and return to its owner, and the probabilities are
+recomputed from the saved log-sum-exp.  Inputs come from
+ring_attention_block_amd.synth; expected values from oracle/ only.
+
+Tolerance (max abs error relative to the largest reference magnitude of the
+tensor): fp32 inputs 1e-4; bf16 inputs 2e-2, the bf16 kernels rounding the
+probabilities and dS to bf16 (2^-9 relative per term) before their products,
+as the forward rounds P.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import backward, dense
+from ring_attention_block_amd import _lib, synth
+from ring_attention_block_amd.ring import RingEmulator
+
+from _helpers import gen_blocks, oracle_values, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    _lib.lib()
+
+
+def _rel_tol(wl):
+    return 2e-2 if wl.dtype == "bf16" else 1e-4
+
+
+def _close(got, want, wl, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    scale = max(float(np.max(np.abs(want))), 1e-30)
+    err = float(np.max(np.abs(got - want)))
+    assert err <= _rel_tol(wl) * scale, f"{what}: max abs error {err:.3e} > {_rel_tol(wl):.0e} x {scale:.3e}"
+    return err / scale
+
+
+def _inputs(wl):
+    jobs = [(r, j) for j in range(wl.blocks)
+            for r in (synth.ROLE_Q, synth.ROLE_K, synth.ROLE_V, synth.ROLE_DO)]
+    host = gen_blocks(wl, jobs)
+    dev = {key: to_device(x, wl) for key, x in host.items()}
+    f64 = {key: oracle_values(x, wl) for key, x in host.items()}
+    return host, dev, f64
+
+
+SMALL = [
+    # (heads, head_dim, rows, blocks, dtype)
+    (2, 128, 200, 3, "bf16"),
+    (1, 64, 130, 3, "f32"),
+    (2, 64, 96, 2, "bf16"),
+    (1, 128, 64, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL)
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_step_every_pair(heads, d, rows, P, dtype, causal):
+    """Each (query block i, key block j) step against the oracle's per-block
+    contribution, both fed the oracle's LSE and D."""
+    wl = synth.Workload(f"bwd_{dtype}_h{heads}_d{d}_c{rows}_p{P}", 400 + rows + d, heads, d, rows,
+                        P, dtype, causal, tuple(range(P)))
+    _, dev, f64 = _inputs(wl)
+    kall = np.concatenate([f64[(synth.ROLE_K, j)] for j in range(P)], axis=1)
+    vall = np.concatenate([f64[(synth.ROLE_V, j)] for j in range(P)], axis=1)
+    kpos = np.arange(P * rows)
+    for i in range(P):
+        qpos = dense.ring_positions(i, rows)
+        q64, do64 = f64[(synth.ROLE_Q, i)], f64[(synth.ROLE_DO, i)]
+        o, lse = dense.attention(q64, kall, vall, qpos, kpos, causal, wl.scale)
+        delta = backward.row_dot(do64, o)
+        lse_d = torch.tensor(lse[None], dtype=torch.float32, device="cuda").contiguous()
+        del_d = torch.tensor(delta[None], dtype=torch.float32, device="cuda").contiguous()
+        for j in range(P):
+            shape = dev[(synth.ROLE_Q, i)].shape
+            dq, dk, dv = (torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(3))
+            case = _lib.bwd_step(dev[(synth.ROLE_Q, i)], dev[(synth.ROLE_DO, i)], lse_d, del_d,
+                                 dev[(synth.ROLE_K, j)], dev[(synth.ROLE_V, j)], dq, dk, dv,
+                                 i, j, P, causal, wl.scale)
+            torch.cuda.synchronize()
+            wq, wk, wv = backward.block_backward(q64, f64[(synth.ROLE_K, j)], f64[(synth.ROLE_V, j)],
+                                                 do64, lse, delta, qpos,
+                                                 dense.ring_positions(j, rows), causal, wl.scale)
+            if case == _lib.RA_CASE_SKIP:
+                assert not dq.any() and not dk.any() and not dv.any()
+                assert not wq.any() and not wk.any() and not wv.any()
+                continue
+            what = f"{wl.name} causal={causal} i={i} j={j}"
+            e = [_close(dq[0].cpu().numpy(), wq, wl, what + " dQ"),
+                 _close(dk[0].cpu().numpy(), wk, wl, what + " dK"),
+                 _close(dv[0].cpu().numpy(), wv, wl, what + " dV")]
+            _say(f"  {what}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
+
+
+@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL[:2])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_ring_gives_full_gradients(heads, d, rows, P, dtype, causal):
+    """Every rank's forward ring, then every rank's backward ring (dK, dV of
+    each block staged in, updated and sent on), against the dense gradients of
+    the whole sequence."""
+    wl = synth.Workload(f"bwdring_{dtype}_h{heads}_d{d}_c{rows}_p{P}", 500 + rows + d, heads, d,
+                        rows, P, dtype, causal, tuple(range(P)))
+    _, dev, f64 = _inputs(wl)
+    shape = dev[(synth.ROLE_Q, 0)].shape
+    kv = {j: (dev[(synth.ROLE_K, j)], dev[(synth.ROLE_V, j)]) for j in range(P)}
+    dk = {j: torch.zeros(shape, dtype=torch.float32, device="cuda") for j in range(P)}
+    dv = {j: torch.zeros(shape, dtype=torch.float32, device="cuda") for j in range(P)}
+    fwd = RingEmulator(shape, dev[(synth.ROLE_Q, 0)].dtype)
+    bwd = RingEmulator(shape, dev[(synth.ROLE_Q, 0)].dtype, compute_stream=fwd.compute,
+                       extra_specs=[(shape, torch.float32), (shape, torch.float32)])
+    dq = {}
+    for i in range(P):
+        st = _lib.State(*shape)
+        fwd.run(st, dev[(synth.ROLE_Q, i)], lambda j: kv[j], i, P, causal, wl.scale)
+        o, lse = _lib.finalize(st, torch.float32, fwd.compute)
+        delta = _lib.bwd_prepare(o, dev[(synth.ROLE_DO, i)], stream=fwd.compute)
+        dq[i] = torch.zeros(shape, dtype=torch.float32, device="cuda")
+        bwd.run_backward(dev[(synth.ROLE_Q, i)], dev[(synth.ROLE_DO, i)], lse, delta, dq[i],
+                         lambda j: (kv[j][0], kv[j][1], dk[j], dv[j]), i, P, causal, wl.scale)
+    torch.cuda.synchronize()
+    cat = lambda role: np.concatenate([f64[(role, j)] for j in range(P)], axis=1)
+    pos = np.arange(P * rows)
+    wq, wk, wv = backward.attention_backward(cat(synth.ROLE_Q), cat(synth.ROLE_K), cat(synth.ROLE_V),
+                                             cat(synth.ROLE_DO), pos, pos, causal, wl.scale)
+    for j in range(P):
+        sl = slice(j * rows, (j + 1) * rows)
+        what = f"{wl.name} causal={causal} block {j}"
+        e = [_close(dq[j][0].cpu().numpy(), wq[:, sl], wl, what + " dQ"),
+             _close(dk[j][0].cpu().numpy(), wk[:, sl], wl, what + " dK"),
+             _close(dv[j][0].cpu().numpy(), wv[:, sl], wl, what + " dV")]
+        _say(f"  {what}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
