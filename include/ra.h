@@ -48,7 +48,8 @@ extern "C" {
 typedef enum {
   RA_OK = 0,
   RA_ERR_INVALID_ARG = -1,  /* bad shape, index, pointer, alignment or scale   */
-  RA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, kv_rows)   */
+  RA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, kv_rows,
+                               bf16 blocks over 2^31 bytes per (batch, head)) */
   RA_ERR_HIP = -3           /* HIP refused to enqueue a kernel or copy         */
 } ra_status;
 
@@ -117,7 +118,8 @@ int32_t ra_step_case(int32_t q_block, int32_t kv_block, int32_t num_blocks, int3
  *              positions are q_block*rows + r and kv_block*rows + t.
  *   scale      score multiplier, finite and > 0 (1/sqrt(head_dim) normally).
  * bf16 inputs use the MFMA path (fp32 accumulation, P rounded to bf16 before
- * the P V product); f32 inputs use an fp32 path.  A skipped block returns
+ * the P V product) and are limited to 2^31 bytes per (batch, head) block of
+ * q, k or v (else RA_ERR_UNSUPPORTED); f32 inputs use an fp32 path.  A skipped block returns
  * RA_OK and enqueues nothing, leaving the state bit-identical.
  */
 ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
@@ -195,9 +197,13 @@ ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t hea
  *   dk, dv    [batch, heads, rows, head_dim] fp32, accumulated (block j)
  *   q_block, kv_block, num_blocks, causal, scale   as in ra_step.
  * The caller zeroes the accumulators before a ring.  A skipped block returns
- * RA_OK and enqueues nothing.  dk and dv are updated with fp32 atomics where
- * several query tiles add to the same keys, so their low bits may differ
- * between runs; dq is written by one workgroup per row.
+ * RA_OK and enqueues nothing.  bf16 inputs with head_dim 128 use the MFMA
+ * path: two kernels (query-stationary for dq, key-stationary for dk and dv),
+ * fp32 accumulation, P and dS rounded to bf16 before their products; each
+ * output row is updated by one workgroup, so results are run-to-run
+ * identical.  Other inputs use an fp32-arithmetic kernel that adds dk and dv
+ * with fp32 atomics (low bits may differ between runs).  bf16 blocks are
+ * limited as in ra_step.
  */
 ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim, const void *q,
                       const void *dout, const float *lse, const float *delta, const void *k,

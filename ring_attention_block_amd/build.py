@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libra.so")
 ARCH = "gfx950"
 
 SOURCES = ["ra_host.hip", "ra_state.hip", "ra_stage.hip", "ra_step_f32.hip", "ra_step_bf16.hip",
-           "ra_bwd.hip"]
+           "ra_bwd.hip", "ra_bwd_bf16.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -66,6 +66,12 @@ ra_status check_state(const ra_state *st, const char *name, int64_t *n_rows) {
   return RA_OK;
 }
 
+// The bf16 kernels address a (batch, head) block through a buffer resource
+// whose byte range and offsets are 32-bit.
+bool bf16_block_too_long(int64_t rows, int32_t head_dim) {
+  return rows * head_dim * 2 > ((int64_t)1 << 31);
+}
+
 ra_status hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess)
     return fail(RA_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
@@ -128,6 +134,8 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
                 kv_rows, st->rows);
   if ((int64_t)st->batch * st->heads * kv_rows > ((int64_t)1 << 40) / st->head_dim)
     return fail(RA_ERR_INVALID_ARG, "ra_step: key/value block of %d rows is too large", kv_rows);
+  if (in_dtype == RA_BF16 && bf16_block_too_long(st->rows > kv_rows ? st->rows : kv_rows, st->head_dim))
+    return fail(RA_ERR_UNSUPPORTED, "ra_step: bf16 blocks are limited to 2^31 bytes per (batch, head)");
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(RA_ERR_INVALID_ARG, "ra_step: scale=%g must be finite and > 0", (double)scale);
   if (n > 0) {
@@ -224,6 +232,8 @@ ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_d
   if (c < 0) return (ra_status)c;
   if (in_dtype != RA_F32 && in_dtype != RA_BF16)
     return fail(RA_ERR_INVALID_ARG, "ra_bwd_step: in_dtype=%d is not RA_F32 or RA_BF16", (int)in_dtype);
+  if (in_dtype == RA_BF16 && bf16_block_too_long(rows, head_dim))
+    return fail(RA_ERR_UNSUPPORTED, "ra_bwd_step: bf16 blocks are limited to 2^31 bytes per (batch, head)");
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(RA_ERR_INVALID_ARG, "ra_bwd_step: scale=%g must be finite and > 0", (double)scale);
   if (n > 0) {
@@ -250,8 +260,10 @@ ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_d
   a.scale_log2 = scale * 1.442695040888963407f;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
   (void)hipGetLastError();
-  return hip_status(ra::launch_bwd_step_simple(a, head_dim, in_dtype == RA_BF16, sc, stream),
-                    "ra_bwd_step launch");
+  const hipError_t e = (in_dtype == RA_BF16 && head_dim == 128)
+                          ? ra::launch_bwd_step_bf16(a, head_dim, sc, stream)
+                          : ra::launch_bwd_step_simple(a, head_dim, in_dtype == RA_BF16, sc, stream);
+  return hip_status(e, "ra_bwd_step launch");
 }
 
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream) {

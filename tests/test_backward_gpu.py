@@ -65,11 +65,15 @@ def _inputs(wl):
 
 
 SMALL = [
-    # (heads, head_dim, rows, blocks, dtype)
+    # (heads, head_dim, rows, blocks, dtype); bf16 with head_dim 128 runs the
+    # matrix-core kernels, the others the general kernel.
     (2, 128, 200, 3, "bf16"),
     (1, 64, 130, 3, "f32"),
+    (8, 128, 640, 2, "bf16"),
+    (16, 128, 1000, 2, "bf16"),
     (2, 64, 96, 2, "bf16"),
     (1, 128, 64, 2, "f32"),
+    (1, 128, 1, 2, "bf16"),
 ]
 
 
@@ -112,7 +116,7 @@ def test_bwd_step_every_pair(heads, d, rows, P, dtype, causal):
             _say(f"  {what}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
 
 
-@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL[:2])
+@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL[:4])
 @pytest.mark.parametrize("causal", [True, False])
 def test_backward_ring_gives_full_gradients(heads, d, rows, P, dtype, causal):
     """Every rank's forward ring, then every rank's backward ring (dK, dV of
@@ -149,3 +153,50 @@ def test_backward_ring_gives_full_gradients(heads, d, rows, P, dtype, causal):
              _close(dk[j][0].cpu().numpy(), wk[:, sl], wl, what + " dK"),
              _close(dv[j][0].cpu().numpy(), wv[:, sl], wl, what + " dV")]
         _say(f"  {what}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
+
+
+@pytest.mark.parametrize("kv_block", [3, 7])
+def test_bwd_step_headline_shape_sampled_heads(kv_block):
+    """The step at the full size of the causal workload (32 heads, head_dim
+    128, 4096 rows per block, query block 7 of 8) against the oracle on two
+    whole heads.  LSE and D are those of attention over block kv_block alone
+    (valid inputs of one step: P is then that block's softmax); the other
+    heads get an upper bound of each row's scaled scores as LSE (P <= 1) and
+    D = 0, so that every workgroup of the launch runs on finite data."""
+    wl = synth.WORKLOADS["causal_bf16_h32_d128_c4096_p8"]
+    i, j, heads = 7, kv_block, (5, 30)
+    host = gen_blocks(wl, [(synth.ROLE_Q, i), (synth.ROLE_DO, i), (synth.ROLE_K, j), (synth.ROLE_V, j)])
+    dev = {key: to_device(x, wl) for key, x in host.items()}
+    f64 = {key: oracle_values(x, wl) for key, x in host.items()}
+    q, do = f64[(synth.ROLE_Q, i)], f64[(synth.ROLE_DO, i)]
+    k, v = f64[(synth.ROLE_K, j)], f64[(synth.ROLE_V, j)]
+    qn = np.linalg.norm(q, axis=2)
+    kmax = np.linalg.norm(k, axis=2).max(axis=1)
+    lse = (wl.scale * qn * kmax[:, None]).astype(np.float32)
+    delta = np.zeros_like(lse)
+    qpos, kpos = dense.ring_positions(i, wl.rows), dense.ring_positions(j, wl.rows)
+    causal = True
+    want = {}
+    for hd in heads:
+        o, l = dense.attention(q[hd:hd + 1], k[hd:hd + 1], v[hd:hd + 1], qpos, kpos, causal, wl.scale)
+        dl = backward.row_dot(do[hd:hd + 1], o)
+        lse[hd], delta[hd] = l[0], dl[0]
+        want[hd] = backward.block_backward(q[hd:hd + 1], k[hd:hd + 1], v[hd:hd + 1], do[hd:hd + 1],
+                                           l, dl, qpos, kpos, causal, wl.scale)
+    shape = dev[(synth.ROLE_Q, i)].shape
+    dq, dk, dv = (torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(3))
+    lse_d = torch.from_numpy(lse[None]).cuda()
+    del_d = torch.from_numpy(delta[None]).cuda()
+    _say(f"  bwd_step headline shape i={i} j={j}")
+    _lib.bwd_step(dev[(synth.ROLE_Q, i)], dev[(synth.ROLE_DO, i)], lse_d, del_d,
+                  dev[(synth.ROLE_K, j)], dev[(synth.ROLE_V, j)], dq, dk, dv, i, j, wl.blocks, causal,
+                  wl.scale)
+    torch.cuda.synchronize()
+    for t, name in ((dq, "dQ"), (dk, "dK"), (dv, "dV")):
+        assert torch.isfinite(t).all(), f"{name}: non-finite values"
+    for hd in heads:
+        wq, wk, wv = want[hd]
+        e = [_close(dq[0, hd].cpu().numpy(), wq[0], wl, f"head {hd} dQ"),
+             _close(dk[0, hd].cpu().numpy(), wk[0], wl, f"head {hd} dK"),
+             _close(dv[0, hd].cpu().numpy(), wv[0], wl, f"head {hd} dV")]
+        _say(f"  j={j} head {hd}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
