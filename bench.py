@@ -6,6 +6,7 @@ ra_step launch per non-skipped block) and the finalize.  Inputs are seeded
 synthetic blocks already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank I]
+                    [--partition contiguous|zigzag] [--decode-rows R] [--backward]
                     [--no-cpu-baseline]
 
 Prints ONE JSON line.  FLOPs count 4*head_dim per unmasked (query, key) pair
@@ -175,6 +176,99 @@ def bench_decode(args, wl):
     print(json.dumps(line), flush=True)
 
 
+def bench_backward(args, wl, rank):
+    """Backward ring of `rank`: D = rowsum(dO * O) (ra_bwd_prepare), then the P
+    ring steps with dK, dV travelling with the visiting block (staged in,
+    updated, sent on).  The forward that provides O and the LSE runs once,
+    before the timed region.  FLOPs count 10*head_dim per unmasked (query, key)
+    pair per head: the five products of the gradients (S, dP, dV, dQ, dK)."""
+    import torch
+    from ring_attention_block_amd import _lib
+    from ring_attention_block_amd.hip_events import Event
+    from ring_attention_block_amd.ring import RingEmulator
+
+    dev = "cuda"
+    blocks = generate(wl, rank)
+    blocks[(synth.ROLE_DO, rank)] = synth.block(wl, synth.ROLE_DO, rank)
+
+    def to_dev(x):
+        t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if wl.dtype == "bf16" \
+            else torch.from_numpy(x)
+        return t.reshape(1, *x.shape).to(dev)
+
+    q = to_dev(blocks[(synth.ROLE_Q, rank)])
+    do = to_dev(blocks[(synth.ROLE_DO, rank)])
+    kv = {j: (to_dev(blocks[(synth.ROLE_K, j)]), to_dev(blocks[(synth.ROLE_V, j)]))
+          for j in range(wl.blocks)}
+    shape = tuple(q.shape)
+    compute = torch.cuda.Stream()
+    st = _lib.State(*shape, device=dev)
+    fwd = RingEmulator(shape, q.dtype, dev, compute_stream=compute)
+    fwd.run(st, q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale)
+    o, lse = _lib.finalize(st, torch.float32, compute)
+    torch.cuda.synchronize()
+    del st
+    grads = {j: (torch.zeros(shape, dtype=torch.float32, device=dev),
+                 torch.zeros(shape, dtype=torch.float32, device=dev)) for j in range(wl.blocks)}
+    dq = torch.zeros(shape, dtype=torch.float32, device=dev)
+    delta = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    bwd = RingEmulator(shape, q.dtype, dev, compute_stream=compute,
+                       extra_specs=[(shape, torch.float32), (shape, torch.float32)])
+    source = lambda j: (kv[j][0], kv[j][1], grads[j][0], grads[j][1])
+
+    def one_ring(timers=None, pool=None):
+        with torch.cuda.stream(compute):
+            dq.zero_()
+        _lib.bwd_prepare(o, do, delta, stream=compute)
+        bwd.run_backward(q, do, lse, delta, dq, source, rank, wl.blocks, wl.causal, wl.scale,
+                         step_timers=timers, timer_events=pool)
+
+    for _ in range(args.warmup):
+        one_ring()
+    torch.cuda.synchronize()
+    cases = [_lib.step_case(rank, j, wl.blocks, wl.causal) for j in range(wl.blocks)]
+    launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
+    pool = iter([Event(timing=True) for _ in range(2 * launched * args.steps)])
+    timers = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_ring(timers, pool)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed / args.steps * 1e3
+    flops = 10 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank)
+    tflops = flops / (ms / 1e3) / 1e12
+    full = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_FULL]
+    diag = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_DIAG]
+    if full:
+        dom_ms, dom_flops = float(np.mean(full)), 10 * wl.head_dim * wl.heads * wl.rows * wl.rows
+        dom = "ra_bwd_step full (bwd_dq + bwd_dkdv kernels)"
+    else:
+        dom_ms = float(np.mean(diag))
+        dom_flops = 10 * wl.head_dim * wl.heads * (wl.rows * (wl.rows + 1) // 2)
+        dom = "ra_bwd_step diagonal (bwd_dq + bwd_dkdv kernels)"
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
+    achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    line = {
+        "metric": "causal bf16 ring-step attention backward TFLOP/s (c=4096, d=128)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
+        "config": {"workload": wl.name, "mode": "backward", "rank": rank, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "rows_per_block": wl.rows, "blocks": wl.blocks,
+                   "causal": wl.causal, "tokens": wl.tokens, "flop_per_step": flops,
+                   "pct_of_mfma_peak": round(100 * tflops / peak, 2)},
+        "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "kernel": dom,
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(dom_ms, 5),
+                     "launches": len(full) if full else len(diag),
+                     "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +283,9 @@ def main():
                     help="instead of the ring: decode this many query rows against the "
                          "workload's P blocks as key/value shards (local fold per shard, "
                          "tree of merges, finalize)")
+    ap.add_argument("--backward", action="store_true",
+                    help="instead of the forward ring: the rank's backward ring (D, then the "
+                         "P gradient steps with dK, dV travelling with the blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -215,6 +312,9 @@ def main():
         return
     rank = args.rank if args.rank is not None else (
         DEFAULT_RANK if wl.name == DEFAULT_WORKLOAD else wl.ranks[-1])
+    if args.backward:
+        bench_backward(args, wl, rank)
+        return
     dev = "cuda"
     compute = torch.cuda.Stream()
 

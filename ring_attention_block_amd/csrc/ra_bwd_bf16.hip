@@ -37,8 +37,8 @@
 //    of 0..7 modulo 8 over each aligned 8), and the transposing reads
 //    ds_read_b64_tr_b16 of 4 consecutive rows x 64 bytes (the four rows land in
 //    four different 64-byte quads, and in distinct halves of 128 bytes).
-//  * tiles are copied HBM -> LDS by buffer loads with an LDS destination,
-//    double buffered, one barrier per tile.
+//  * tiles are copied HBM -> LDS by buffer loads with an LDS destination
+//    (double buffered in bwd_dq, triple in bwd_dkdv), one barrier per tile.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -331,6 +331,18 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
 }
 
 // ---------------------------------------------------------------- dK, dV ----
+// The two halves of a dK/dV iteration are scheduled as separate regions: the
+// compiler then interleaves each half's softmax with its products instead of
+// hoisting work across the halves and raising register pressure.
+#define RA_DKDV_HALF_END() __builtin_amdgcn_sched_barrier(0)
+// One wavefront per SIMD (the dK^T and dV^T accumulators take 128 registers
+// beside the 64 of K and V), so the work is software-pipelined by 32-query
+// sub-tiles instead of relying on a second wavefront: while the matrix cores
+// run the dV/dK products of sub-tile n and the S/dP products of sub-tile n+1,
+// the vector unit turns the S/dP of sub-tile n into P and dS.  A tile is read
+// from the iteration before it is current until the end of its own iteration,
+// so query tiles are triple buffered: iteration u computes on tiles u and u+1
+// while tile u+2 is copied in.
 template <int D, bool kDiag>
 __global__ void __launch_bounds__(64 * kWaves, 1) bwd_dkdv_bf16_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -339,12 +351,14 @@ __global__ void __launch_bounds__(64 * kWaves, 1) bwd_dkdv_bf16_kernel(BwdArgs a
   constexpr int kQK = D / 16, kDB = D / 32;
   __shared__ __attribute__((aligned(1024))) char lds_q0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_q1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_q2[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_o0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char lds_o1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_o2[T::kBytes];
   // Per query of a tile: -LSE * log2(e) (-inf for a row past the end or one
   // that saw no key) and D.
-  __shared__ __attribute__((aligned(16))) float lds_nl[2][kBT];
-  __shared__ __attribute__((aligned(16))) float lds_dd[2][kBT];
+  __shared__ __attribute__((aligned(16))) float lds_nl[3][kBT];
+  __shared__ __attribute__((aligned(16))) float lds_dd[3][kBT];
 
   const int rows = a.rows;
   const int n_kt = (rows + kBK - 1) / kBK;
@@ -364,26 +378,35 @@ __global__ void __launch_bounds__(64 * kWaves, 1) bwd_dkdv_bf16_kernel(BwdArgs a
   uint32_t coff[T::kLoadsPerWave];
   copy_offsets<D>(coff, wave, lane);
 
-  const int first = kDiag ? (kt * kBK) / kBT : 0;   // queries before the workgroup's keys see none of them
-  const int n_all = (rows + kBT - 1) / kBT;
-  const int last = n_all - 1;
-  if (last - first <= 1 && last * kBT + kBT > rows) {
-    const bool odd = (last - first) & 1;
-    zero_tail<D>(odd ? lds_q1 : lds_q0, odd ? lds_o1 : lds_o0, rows - last * kBT, tid);
+  // Query tiles first .. first+n-1; tile first+u lives in buffer u % 3.
+  const int first = kDiag ? (kt * kBK) / kBT : 0;   // earlier queries see none of the keys
+  const int n = (rows + kBT - 1) / kBT - first;
+  auto qbuf = [&](int i) { return i == 0 ? lds_q0 : (i == 1 ? lds_q1 : lds_q2); };
+  auto obuf = [&](int i) { return i == 0 ? lds_o0 : (i == 1 ? lds_o1 : lds_o2); };
+  {
+    const int last = first + n - 1;
+    if (n <= 3 && last * kBT + kBT > rows)
+      zero_tail<D>(qbuf((n - 1) % 3), obuf((n - 1) % 3), rows - last * kBT, tid);
   }
+  // Thread tid < 64 stages -LSE*log2(e) of query tid of a tile, 64 <= tid < 128
+  // its D.  The load is branch-free (clamped row) and its value is used only
+  // by the store at the end of the iteration, so that waiting for it does not
+  // also wait for the tile copies issued before it.
+  const float *stage_src = (tid < kBT ? a.lse : a.delta) + sbase;
+  auto stage_load = [&](int tile) { return stage_src[min(tile * kBT + (tid & 63), rows - 1)]; };
+  auto stage_store = [&](int buf, int tile, float raw) {
+    const bool ok = tile * kBT + (tid & 63) < rows;
+    if (tid < kBT) lds_nl[buf][tid] = ok ? neg_lse2(raw) : -INFINITY;
+    else if (tid < 2 * kBT) lds_dd[buf][tid - kBT] = ok ? raw : 0.f;
+  };
   issue_copy<D>(lds_q0, rq, coff, first * kBT, wave);
   issue_copy<D>(lds_o0, ro, coff, first * kBT, wave);
-  // Thread tid < 64 stages -LSE*log2(e) of query tid of a tile, 64 <= tid < 128 its D.
-  auto stage_load = [&](int tile) {
-    const int q = tile * kBT + (tid & 63);
-    if (tid >= 2 * kBT || q >= rows) return tid < kBT ? -INFINITY : 0.f;
-    return tid < kBT ? neg_lse2(a.lse[sbase + q]) : a.delta[sbase + q];
-  };
-  auto stage_store = [&](int buf, float x) {
-    if (tid < kBT) lds_nl[buf][tid] = x;
-    else if (tid < 2 * kBT) lds_dd[buf][tid - kBT] = x;
-  };
-  stage_store(0, stage_load(first));
+  stage_store(0, first, stage_load(first));
+  if (n > 1) {
+    issue_copy<D>(lds_q1, rq, coff, (first + 1) * kBT, wave);
+    issue_copy<D>(lds_o1, ro, coff, (first + 1) * kBT, wave);
+    stage_store(1, first + 1, stage_load(first + 1));
+  }
 
   // B operands: lane (r, h) holds k[key][16c + 8h ..] and v[key][16c + 8h ..].
   bf16x8 kf[kQK], vf[kQK];
@@ -406,70 +429,108 @@ __global__ void __launch_bounds__(64 * kWaves, 1) bwd_dkdv_bf16_kernel(BwdArgs a
   const FragOffsets<D> fo = frag_offsets<D>(lane);
   const float sl2 = a.scale_log2;
 
-  auto body = [&](int t, int buf, const char *qb, const char *ob) {
-    const bool masked = kDiag && t * kBT < k0w + 31;   // some query of the tile precedes some key
+  // Sub-tile (tile t, half sb) covers queries 64t + 32sb .. +31.
+  auto skipped = [&](int t, int sb) { return kDiag && t * kBT + sb * 32 + 31 < k0w; };
+  auto needs_mask = [&](int t, int sb) { return kDiag && t * kBT + sb * 32 < k0w + 31; };
+  // S = Q K^T and dP = dO V^T of a sub-tile: entry i of lane (key, h) is query
+  // 32sb + 16(i/8) + 8h + i%8 of the tile.
+  auto sdp = [&](const char *qb, const char *ob, int sb, f32x16 &s, f32x16 &dp) {
+    s = f32x16{};
+    dp = f32x16{};
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int c = 0; c < kQK; ++c) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_nrm<D>(qb, fo, sb, c), kf[c], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_nrm<D>(ob, fo, sb, c), vf[c], dp, 0, 0, 0);
-      }
-      // s[i], dp[i]: query t*64 + 32sb + 16(i/8) + 8h + i%8 against this lane's key.
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int q0 = sb * 32 + hh * 16 + 8 * h;
-        const float4 n0 = *(const lds_float4 *)&lds_nl[buf][q0];
-        const float4 n1 = *(const lds_float4 *)&lds_nl[buf][q0 + 4];
-        const float4 d0 = *(const lds_float4 *)&lds_dd[buf][q0];
-        const float4 d1 = *(const lds_float4 *)&lds_dd[buf][q0 + 4];
-        const float nl[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
-        const float dl[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = hh * 8 + e;
-          float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nl[e]));
-          if (masked) p = t * kBT + q0 + e < key ? 0.f : p;
-          pb[hh][e] = (__bf16)p;
-          dsb[hh][e] = (__bf16)(p * (dp[i] - dl[e]));
-        }
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int b = 0; b < kDB; ++b) {
-          dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ob, fo, 2 * sb + half, b), pb[half],
-                                                          dv[b], 0, 0, 0);
-          dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(qb, fo, 2 * sb + half, b), dsb[half],
-                                                          dk[b], 0, 0, 0);
-        }
+    for (int c = 0; c < kQK; ++c) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_nrm<D>(qb, fo, sb, c), kf[c], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_nrm<D>(ob, fo, sb, c), vf[c], dp, 0, 0, 0);
     }
   };
-  auto iteration = [&](int t, int buf, char *q_dst, char *o_dst, const char *q_src, const char *o_src) {
-    const bool has_next = t + 1 < n_all;
-    float staged = 0.f;
-    if (has_next) {
-      issue_copy<D>(q_dst, rq, coff, (t + 1) * kBT, wave);
-      issue_copy<D>(o_dst, ro, coff, (t + 1) * kBT, wave);
-      staged = stage_load(t + 1);
+  // P and dS of a sub-tile as the B operands of the gradient products.
+  auto softmax = [&](const f32x16 &s, const f32x16 &dp, int buf, int t, int sb, bf16x8 (&pb)[2],
+                     bf16x8 (&dsb)[2]) {
+    const bool masked = needs_mask(t, sb);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int q0 = sb * 32 + hh * 16 + 8 * h;
+      const float4 n0 = *(const lds_float4 *)&lds_nl[buf][q0];
+      const float4 n1 = *(const lds_float4 *)&lds_nl[buf][q0 + 4];
+      const float4 d0 = *(const lds_float4 *)&lds_dd[buf][q0];
+      const float4 d1 = *(const lds_float4 *)&lds_dd[buf][q0 + 4];
+      const float nl[8] = {n0.x, n0.y, n0.z, n0.w, n1.x, n1.y, n1.z, n1.w};
+      const float dl[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = hh * 8 + e;
+        float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nl[e]));
+        if (masked) p = t * kBT + q0 + e < key ? 0.f : p;
+        pb[hh][e] = (__bf16)p;
+        dsb[hh][e] = (__bf16)(p * (dp[i] - dl[e]));
+      }
     }
-    if (!(kDiag && t * kBT + kBT - 1 < k0w)) body(t, buf, q_src, o_src);
-    if (has_next) stage_store(buf ^ 1, staged);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries.
+  auto grads = [&](const char *qb, const char *ob, int sb, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int b = 0; b < kDB; ++b) {
+        dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(ob, fo, 2 * sb + half, b), pb[half],
+                                                        dv[b], 0, 0, 0);
+        dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(qb, fo, 2 * sb + half, b), dsb[half],
+                                                        dk[b], 0, 0, 0);
+      }
   };
 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int t = first;
+  f32x16 s0, dp0;   // S, dP of sub-tile (current tile, 0)
+  if (!skipped(first, 0)) sdp(lds_q0, lds_o0, 0, s0, dp0);
+
+  // Iteration u: tile t = first + u in buffer bc, tile t+1 in b1, copies of
+  // tile t+2 into b2.
+  auto iteration = [&](int u, int bc, int b1, int b2, const char *qc, const char *oc, const char *q1,
+                       const char *o1, char *q2, char *o2) {
+    const int t = first + u;
+    float staged = 0.f;
+    if (u + 2 < n) {
+      issue_copy<D>(q2, rq, coff, (t + 2) * kBT, wave);
+      issue_copy<D>(o2, ro, coff, (t + 2) * kBT, wave);
+      staged = stage_load(t + 2);
+    }
+    f32x16 s1, dp1;
+    bf16x8 pb[2], dsb[2];
+    if (!kDiag) {
+      // First half: P, dS of (t, 0); S, dP of (t, 1); gradients of (t, 0).
+      softmax(s0, dp0, bc, t, 0, pb, dsb);
+      sdp(qc, oc, 1, s1, dp1);
+      grads(qc, oc, 0, pb, dsb);
+      RA_DKDV_HALF_END();
+      // Second half: P, dS of (t, 1); S, dP of (t+1, 0) (stale and unused
+      // after the last tile); gradients of (t, 1).
+      softmax(s1, dp1, bc, t, 1, pb, dsb);
+      sdp(q1, o1, 0, s0, dp0);
+      grads(qc, oc, 1, pb, dsb);
+      RA_DKDV_HALF_END();
+    } else {
+      if (!skipped(t, 0)) softmax(s0, dp0, bc, t, 0, pb, dsb);
+      if (!skipped(t, 1)) sdp(qc, oc, 1, s1, dp1);
+      if (!skipped(t, 0)) grads(qc, oc, 0, pb, dsb);
+      if (!skipped(t, 1)) softmax(s1, dp1, bc, t, 1, pb, dsb);
+      if (u + 1 < n && !skipped(t + 1, 0)) sdp(q1, o1, 0, s0, dp0);
+      if (!skipped(t, 1)) grads(qc, oc, 1, pb, dsb);
+    }
+    if (u + 2 < n) stage_store(b2, t + 2, staged);
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of tile t+2 landed
+    __syncthreads();
+  };
+
+  int u = 0;
 #pragma clang loop unroll(disable)
-  for (; t + 1 < n_all; t += 2) {
-    iteration(t, 0, lds_q1, lds_o1, lds_q0, lds_o0);
-    iteration(t + 1, 1, lds_q0, lds_o0, lds_q1, lds_o1);
+  for (; u + 2 < n; u += 3) {
+    iteration(u, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
+    iteration(u + 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
+    iteration(u + 2, 2, 0, 1, lds_q2, lds_o2, lds_q0, lds_o0, lds_q1, lds_o1);
   }
-  if (t < n_all) iteration(t, 0, lds_q1, lds_o1, lds_q0, lds_o0);
+  if (u < n) iteration(u, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
+  if (u + 1 < n) iteration(u + 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
 
   if (key_ok) {
     add_row<D>(a.dk + base + (size_t)key * D, dk, h, a.scale);
