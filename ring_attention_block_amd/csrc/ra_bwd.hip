@@ -31,19 +31,27 @@ __device__ __forceinline__ float load_elem(const uint16_t *p, size_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }
 
-// D[row] = sum_x dO[row][x] * O[row][x]; one thread per row.
+// D[row] = sum_x dO[row][x] * O[row][x].  Sixteen lanes per row: in step i
+// lane l reads column 16i + l, so each step reads a contiguous run of the row;
+// the partial sums are combined across the 16 lanes.
 template <int D, typename OT, typename DT>
 __global__ void __launch_bounds__(256) bwd_prepare_kernel(const OT *__restrict__ o,
                                                           const DT *__restrict__ dout,
                                                           float *__restrict__ delta,
                                                           int64_t n_rows) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= n_rows) return;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
   float acc = 0.f;
-#pragma unroll 8
-  for (int x = 0; x < D; ++x)
-    acc = fmaf(load_elem(dout, (size_t)row * D + x), load_elem(o, (size_t)row * D + x), acc);
-  delta[row] = acc;
+  if (row < n_rows) {
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i)
+      acc = fmaf(load_elem(dout, (size_t)row * D + 16 * i + l), load_elem(o, (size_t)row * D + 16 * i + l), acc);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  acc += __shfl_xor(acc, 8);
+  if (row < n_rows && l == 0) delta[row] = acc;
 }
 
 constexpr int kRows = 64;     // query rows per workgroup
@@ -158,7 +166,7 @@ hipError_t launch_simple_d(const BwdArgs &a, bool diag, hipStream_t s) {
 template <int D>
 hipError_t launch_prepare_d(const void *o, bool o_bf16, const void *dout, bool do_bf16,
                             float *delta, int64_t n_rows, hipStream_t s) {
-  const dim3 grid((unsigned)((n_rows + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
   const float *of = static_cast<const float *>(o);
   const uint16_t *ob = static_cast<const uint16_t *>(o);
   const float *df = static_cast<const float *>(dout);

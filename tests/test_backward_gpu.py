@@ -200,3 +200,21 @@ def test_bwd_step_headline_shape_sampled_heads(kv_block):
              _close(dk[0, hd].cpu().numpy(), wk[0], wl, f"head {hd} dK"),
              _close(dv[0, hd].cpu().numpy(), wv[0], wl, f"head {hd} dV")]
         _say(f"  j={j} head {hd}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
+
+
+@pytest.mark.parametrize("heads,d,rows,o_dtype,do_dtype", [
+    (3, 128, 37, "f32", "bf16"), (2, 64, 100, "bf16", "bf16"), (1, 128, 1, "f32", "f32"),
+    (32, 128, 4096, "f32", "bf16")])
+def test_bwd_prepare_row_dot(heads, d, rows, o_dtype, do_dtype):
+    """ra_bwd_prepare against the oracle's D = rowsum(dO * O) (fp32 sums of
+    products of exactly representable inputs: relative error ~ d * 2^-24)."""
+    wl_o = synth.Workload("prep_o", 71 + rows, heads, d, rows, 1, o_dtype, False, (0,))
+    wl_d = synth.Workload("prep_do", 72 + rows, heads, d, rows, 1, do_dtype, False, (0,))
+    o_h = synth.block(wl_o, synth.ROLE_Q, 0)
+    d_h = synth.block(wl_d, synth.ROLE_DO, 0)
+    got = _lib.bwd_prepare(to_device(o_h, wl_o), to_device(d_h, wl_d))
+    torch.cuda.synchronize()
+    want = backward.row_dot(oracle_values(d_h, wl_d), oracle_values(o_h, wl_o))
+    bound = np.sum(np.abs(oracle_values(d_h, wl_d) * oracle_values(o_h, wl_o)), axis=-1)
+    err = np.abs(got[0].cpu().numpy().astype(np.float64) - want)
+    assert np.all(err <= 1e-6 * d * bound + 1e-30), float(np.max(err / (bound + 1e-30)))
