@@ -67,18 +67,20 @@ def generate(wl, rank, threads=16, q_blocks=None):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                "ra_step_bf16_full_causal_h32_d128_c4096_hbm_traffic.md")
+BWD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                                   "ra_bwd_step_bf16_full_causal_h32_d128_c4096_hbm_traffic.md")
 
 
-def measured_traffic(wl):
-    """HBM bytes per full-step launch from the committed FETCH_SIZE/WRITE_SIZE summary.
+def measured_traffic(wl, profile=TRAFFIC_PROFILE):
+    """HBM bytes per full-step launch from a committed FETCH_SIZE/WRITE_SIZE summary.
 
     Only for the workload the counters were taken on, and only while the
     kernel source still hashes to the value recorded with them; else None.
     """
-    if wl.name != DEFAULT_WORKLOAD or not os.path.exists(TRAFFIC_PROFILE):
+    if wl.name != DEFAULT_WORKLOAD or not os.path.exists(profile):
         return None
     fields = {}
-    for line in open(TRAFFIC_PROFILE):
+    for line in open(profile):
         key, sep, val = line.strip().partition(": ")
         if sep and key in ("traffic_bytes_per_launch", "kernel_source", "kernel_source_sha256"):
             fields[key] = val.strip()
@@ -261,7 +263,8 @@ def bench_backward(args, wl, rank):
                    "pct_of_mfma_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "kernel": dom,
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(wl, BWD_TRAFFIC_PROFILE) if full else None,
                      "avg_launch_ms": round(dom_ms, 5),
                      "launches": len(full) if full else len(diag),
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
