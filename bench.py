@@ -187,48 +187,69 @@ def bench_backward(args, wl, rank):
     import torch
     from ring_attention_block_amd import _lib
     from ring_attention_block_amd.hip_events import Event
-    from ring_attention_block_amd.ring import RingEmulator
+    from ring_attention_block_amd.ring import RingEmulator, ZigzagRing, zigzag_blocks, zigzag_plan
 
     dev = "cuda"
-    blocks = generate(wl, rank)
-    blocks[(synth.ROLE_DO, rank)] = synth.block(wl, synth.ROLE_DO, rank)
+    zigzag = args.partition == "zigzag"
+    step_wl = synth.zigzag_workload(wl) if zigzag else wl
+    mine = zigzag_blocks(rank, wl.blocks) if zigzag else (rank,)
+    blocks = generate(step_wl, rank, q_blocks=mine)
+    for b in mine:
+        blocks[(synth.ROLE_DO, b)] = synth.block(step_wl, synth.ROLE_DO, b)
 
     def to_dev(x):
         t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if wl.dtype == "bf16" \
             else torch.from_numpy(x)
         return t.reshape(1, *x.shape).to(dev)
 
-    q = to_dev(blocks[(synth.ROLE_Q, rank)])
-    do = to_dev(blocks[(synth.ROLE_DO, rank)])
+    qs = [to_dev(blocks[(synth.ROLE_Q, b)]) for b in mine]
+    dos = [to_dev(blocks[(synth.ROLE_DO, b)]) for b in mine]
     kv = {j: (to_dev(blocks[(synth.ROLE_K, j)]), to_dev(blocks[(synth.ROLE_V, j)]))
-          for j in range(wl.blocks)}
-    shape = tuple(q.shape)
+          for j in range(step_wl.blocks)}
+    shape = tuple(qs[0].shape)
     compute = torch.cuda.Stream()
-    st = _lib.State(*shape, device=dev)
-    fwd = RingEmulator(shape, q.dtype, dev, compute_stream=compute)
-    fwd.run(st, q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale)
-    o, lse = _lib.finalize(st, torch.float32, compute)
-    torch.cuda.synchronize()
-    del st
+    states = [_lib.State(*shape, device=dev) for _ in mine]
     grads = {j: (torch.zeros(shape, dtype=torch.float32, device=dev),
-                 torch.zeros(shape, dtype=torch.float32, device=dev)) for j in range(wl.blocks)}
-    dq = torch.zeros(shape, dtype=torch.float32, device=dev)
-    delta = torch.empty(shape[:3], dtype=torch.float32, device=dev)
-    bwd = RingEmulator(shape, q.dtype, dev, compute_stream=compute,
-                       extra_specs=[(shape, torch.float32), (shape, torch.float32)])
-    source = lambda j: (kv[j][0], kv[j][1], grads[j][0], grads[j][1])
+                 torch.zeros(shape, dtype=torch.float32, device=dev)) for j in range(step_wl.blocks)}
+    dqs = [torch.zeros(shape, dtype=torch.float32, device=dev) for _ in mine]
+    deltas = [torch.empty(shape[:3], dtype=torch.float32, device=dev) for _ in mine]
+    if zigzag:
+        ring = ZigzagRing(shape, qs[0].dtype, dev, compute_stream=compute, backward=True)
+
+        def source(j):
+            a, b = zigzag_blocks(j, wl.blocks)
+            return (kv[a][0], kv[b][0], kv[a][1], kv[b][1], grads[a][0], grads[b][0],
+                    grads[a][1], grads[b][1])
+
+        ring.run(states, qs, lambda j: source(j)[:4], rank, wl.blocks, wl.causal, wl.scale)
+        cases = [c for _, prods in zigzag_plan(rank, wl.blocks, wl.causal) for _, _, c in prods]
+    else:
+        ring = RingEmulator(shape, qs[0].dtype, dev, compute_stream=compute,
+                            extra_specs=[(shape, torch.float32), (shape, torch.float32)])
+        source = lambda j: (kv[j][0], kv[j][1], grads[j][0], grads[j][1])
+        ring.run(states[0], qs[0], lambda j: source(j)[:2], rank, wl.blocks, wl.causal, wl.scale)
+        cases = [_lib.step_case(rank, j, wl.blocks, wl.causal) for j in range(wl.blocks)]
+    outs = [_lib.finalize(st, torch.float32, compute) for st in states]
+    torch.cuda.synchronize()
+    del states
 
     def one_ring(timers=None, pool=None):
         with torch.cuda.stream(compute):
-            dq.zero_()
-        _lib.bwd_prepare(o, do, delta, stream=compute)
-        bwd.run_backward(q, do, lse, delta, dq, source, rank, wl.blocks, wl.causal, wl.scale,
-                         step_timers=timers, timer_events=pool)
+            for dq in dqs:
+                dq.zero_()
+        for (o, _), do, delta in zip(outs, dos, deltas):
+            _lib.bwd_prepare(o, do, delta, stream=compute)
+        lses = [lse for _, lse in outs]
+        if zigzag:
+            ring.run_backward(qs, dos, lses, deltas, dqs, source, rank, wl.blocks, wl.causal,
+                              wl.scale, step_timers=timers, timer_events=pool)
+        else:
+            ring.run_backward(qs[0], dos[0], lses[0], deltas[0], dqs[0], source, rank, wl.blocks,
+                              wl.causal, wl.scale, step_timers=timers, timer_events=pool)
 
     for _ in range(args.warmup):
         one_ring()
     torch.cuda.synchronize()
-    cases = [_lib.step_case(rank, j, wl.blocks, wl.causal) for j in range(wl.blocks)]
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
     pool = iter([Event(timing=True) for _ in range(2 * launched * args.steps)])
     timers = []
@@ -238,16 +259,18 @@ def bench_backward(args, wl, rank):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
-    flops = 10 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank)
+    c2 = step_wl.rows
+    pairs = (cases.count(_lib.RA_CASE_FULL) * c2 * c2 + cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
+    flops = 10 * wl.head_dim * wl.heads * pairs
     tflops = flops / (ms / 1e3) / 1e12
     full = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_FULL]
     diag = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_DIAG]
     if full:
-        dom_ms, dom_flops = float(np.mean(full)), 10 * wl.head_dim * wl.heads * wl.rows * wl.rows
+        dom_ms, dom_flops = float(np.mean(full)), 10 * wl.head_dim * wl.heads * c2 * c2
         dom = "ra_bwd_step full (bwd_dq + bwd_dkdv kernels)"
     else:
         dom_ms = float(np.mean(diag))
-        dom_flops = 10 * wl.head_dim * wl.heads * (wl.rows * (wl.rows + 1) // 2)
+        dom_flops = 10 * wl.head_dim * wl.heads * (c2 * (c2 + 1) // 2)
         dom = "ra_bwd_step diagonal (bwd_dq + bwd_dkdv kernels)"
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
@@ -257,14 +280,16 @@ def bench_backward(args, wl, rank):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
-        "config": {"workload": wl.name, "mode": "backward", "rank": rank, "heads": wl.heads,
+        "config": {"workload": wl.name, "mode": "backward", "rank": rank,
+                   "partition": args.partition, "heads": wl.heads,
                    "head_dim": wl.head_dim, "rows_per_block": wl.rows, "blocks": wl.blocks,
                    "causal": wl.causal, "tokens": wl.tokens, "flop_per_step": flops,
                    "pct_of_mfma_peak": round(100 * tflops / peak, 2)},
         "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "kernel": dom,
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(wl, BWD_TRAFFIC_PROFILE) if full else None,
+                     "traffic": (measured_traffic(wl, BWD_TRAFFIC_PROFILE)
+                                 if full and not zigzag else None),
                      "avg_launch_ms": round(dom_ms, 5),
                      "launches": len(full) if full else len(diag),
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},

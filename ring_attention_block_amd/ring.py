@@ -218,9 +218,13 @@ class ZigzagRing:
     (K_a, K_b, V_a, V_b) of rank j's two sub-blocks zigzag_blocks(j, P).
     """
 
-    def __init__(self, sub_shape, dtype, device="cuda", compute_stream=None, copy_stream=None):
+    def __init__(self, sub_shape, dtype, device="cuda", compute_stream=None, copy_stream=None,
+                 backward: bool = False):
+        # backward: also stage the fp32 dK, dV of the visiting rank's two sub-blocks.
+        extra = [(tuple(sub_shape), torch.float32)] * 4 if backward else ()
         self.emu = RingEmulator(sub_shape, dtype, device, compute_stream, copy_stream,
-                                tensors_per_visit=4)
+                                tensors_per_visit=4, extra_specs=extra)
+        self.backward = backward
 
     @property
     def compute(self):
@@ -245,4 +249,43 @@ class ZigzagRing:
                               2 * ranks, causal, scale, case, step_timers, timer_events)
 
         self.emu.visit([j for j, _ in plan], kv_source, fold)
+        return plan
+
+    def run_backward(self, qs: Sequence[torch.Tensor], douts: Sequence[torch.Tensor],
+                     lses: Sequence[torch.Tensor], deltas: Sequence[torch.Tensor],
+                     dqs: Sequence[torch.Tensor], source: Callable[[int], tuple], rank: int,
+                     ranks: int, causal: bool, scale: float, step_timers: list | None = None,
+                     timer_events=None) -> list:
+        """Backward ring of `rank` under the zigzag partition: the two fp32 dq
+        sub-block tensors (zeroed by the caller) accumulate every visiting
+        sub-block's contribution; source(j) returns (K_a, K_b, V_a, V_b, dK_a,
+        dK_b, dV_a, dV_b) of rank j's sub-blocks zigzag_blocks(j, ranks), whose
+        fp32 dK, dV travel with them (staged in, updated by this rank's piece
+        products, sent on).  Needs backward=True at construction.  Returns
+        zigzag_plan(rank, ranks, causal)."""
+        if not self.backward:
+            raise RuntimeError("ZigzagRing.run_backward needs backward=True at construction")
+        plan = zigzag_plan(rank, ranks, causal)
+        mine = zigzag_blocks(rank, ranks)
+        comp = self.compute
+
+        def fold(s, j, t):
+            theirs = zigzag_blocks(j, ranks)
+            for a, b, case in plan[s][1]:
+                timed = step_timers is not None and case != _lib.RA_CASE_SKIP
+                if timed:
+                    e0 = next(timer_events) if timer_events is not None else Event(timing=True)
+                    e1 = next(timer_events) if timer_events is not None else Event(timing=True)
+                    e0.record(comp)
+                _lib.bwd_step(qs[a], douts[a], lses[a], deltas[a], t[b], t[2 + b], dqs[a],
+                              t[4 + b], t[6 + b], mine[a], theirs[b], 2 * ranks, causal, scale, comp)
+                if timed:
+                    e1.record(comp)
+                    step_timers.append((case, e0, e1))
+
+        def drain(j, t, stream):
+            for dst, src in zip(source(j)[4:8], t[4:8]):
+                _lib.stage_block(dst, src, stream)
+
+        self.emu.visit([j for j, _ in plan], source, fold, drain)
         return plan

@@ -104,3 +104,59 @@ def test_zigzag_headline_shape_sampled_rows():
     for rank in (0, 7):
         _say(f"{sub.name} rank={rank}")
         check_rank(sub, rank, wl.blocks, True, cache, rows=rows)
+
+
+@pytest.mark.parametrize("heads,d,rows,P,dtype", [(2, 128, 400, 3, "bf16"), (1, 64, 128, 4, "f32"),
+                                                 (2, 128, 1024, 2, "bf16")])
+@pytest.mark.parametrize("causal", [True, False])
+def test_zigzag_backward_all_ranks(heads, d, rows, P, dtype, causal):
+    """Every rank's zigzag forward ring, then every rank's zigzag backward ring
+    (the dK, dV of each sub-block travel with it), against the dense gradients
+    of the whole sequence ("Ring Attention：把超长序列沿设备环流动", section
+    "Backward 需要让梯度也沿环传播"); tolerance as in test_backward_gpu.py."""
+    from oracle import backward
+    from _helpers import oracle_values
+    wl = synth.Workload(f"zzb_{dtype}_h{heads}_d{d}_c{rows}_p{P}", 300 + rows + d, heads, d, rows,
+                        P, dtype, causal, tuple(range(P)))
+    sub = synth.zigzag_workload(wl)
+    n = 2 * P
+    host = gen_blocks(sub, [(r, b) for b in range(n)
+                            for r in (synth.ROLE_Q, synth.ROLE_K, synth.ROLE_V, synth.ROLE_DO)])
+    dev = {key: to_device(x, sub) for key, x in host.items()}
+    shape = dev[(synth.ROLE_Q, 0)].shape
+    dk = {b: torch.zeros(shape, dtype=torch.float32, device="cuda") for b in range(n)}
+    dv = {b: torch.zeros(shape, dtype=torch.float32, device="cuda") for b in range(n)}
+    dq = {b: torch.zeros(shape, dtype=torch.float32, device="cuda") for b in range(n)}
+
+    def source(j):
+        a, b = zigzag_blocks(j, P)
+        return (dev[(synth.ROLE_K, a)], dev[(synth.ROLE_K, b)], dev[(synth.ROLE_V, a)],
+                dev[(synth.ROLE_V, b)], dk[a], dk[b], dv[a], dv[b])
+
+    ring = ZigzagRing(shape, dev[(synth.ROLE_Q, 0)].dtype, backward=True)
+    for rank in range(P):
+        mine = zigzag_blocks(rank, P)
+        qs = [dev[(synth.ROLE_Q, b)] for b in mine]
+        dos = [dev[(synth.ROLE_DO, b)] for b in mine]
+        states = [_lib.State(1, heads, sub.rows, d) for _ in range(2)]
+        ring.run(states, qs, lambda j: source(j)[:4], rank, P, causal, sub.scale)
+        outs = [_lib.finalize(st, torch.float32, ring.compute) for st in states]
+        lses = [lse for _, lse in outs]
+        deltas = [_lib.bwd_prepare(o, do, stream=ring.compute) for (o, _), do in zip(outs, dos)]
+        ring.run_backward(qs, dos, lses, deltas, [dq[b] for b in mine], source, rank, P, causal,
+                          sub.scale)
+        torch.cuda.synchronize()
+    cat = lambda role: np.concatenate([oracle_values(host[(role, b)], sub) for b in range(n)], axis=1)
+    pos = np.arange(n * sub.rows)
+    wq, wk, wv = backward.attention_backward(cat(synth.ROLE_Q), cat(synth.ROLE_K), cat(synth.ROLE_V),
+                                             cat(synth.ROLE_DO), pos, pos, causal, sub.scale)
+    rel = 2e-2 if dtype == "bf16" else 1e-4
+    for b in range(n):
+        sl = slice(b * sub.rows, (b + 1) * sub.rows)
+        for got, want, name in ((dq[b], wq, "dQ"), (dk[b], wk, "dK"), (dv[b], wv, "dV")):
+            g = got[0].cpu().numpy().astype(np.float64)
+            w = want[:, sl]
+            scale_ = max(float(np.max(np.abs(want))), 1e-30)
+            err = float(np.max(np.abs(g - w)))
+            assert np.isfinite(g).all() and err <= rel * scale_, (b, name, err, scale_)
+        _say(f"  {sub.name} causal={causal} piece {b} ok")
