@@ -46,6 +46,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ra_kernels.h"
 
 namespace ra {
@@ -430,7 +432,11 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // so that every LDS access names one static buffer:
   //   copies: K(t+2) -> k_dst (= K buffer t%2), V(t+1) -> v_dst (V buffer (t+1)%2)
   //   reads:  K(t+1) <- k_src (K buffer (t+1)%2), V(t) <- v_src (V buffer t%2)
-  auto iteration = [&](int t, char *k_dst, char *v_dst, const char *k_src, const char *v_src) {
+  // `fast` (a compile-time flag): tiles t and t+1 need no mask, so the
+  // iteration is the interleaved block; otherwise the general masked one.
+  auto iteration = [&](auto fast, int t, char *k_dst, char *v_dst, const char *k_src,
+                       const char *v_src) {
+    constexpr bool kFast = decltype(fast)::value;
     if (t + 2 < n_tiles) issue_copy<D, kW>(k_dst, rk, so.k, (t + 2) * kBN, wave);
     if (t + 1 < n_tiles) issue_copy<D, kW>(v_dst, rv, so.v, (t + 1) * kBN, wave);
     const bool has_next = t + 1 < n_tiles;
@@ -439,7 +445,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     bf16x8 pb[4];
     bool rescale = false;
     float alpha = 1.f;
-    if (!kMask) {
+    if constexpr (kFast) {
       // The scores of the tile after the last one read a stale K buffer;
       // has_next = false keeps them out of the state.
       scores(s_nxt, k_src);
@@ -486,13 +492,47 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     __syncthreads();
   };
 
+  using Fast = std::integral_constant<bool, true>;
+  using Masked = std::integral_constant<bool, false>;
   int t = 0;
+  if constexpr (!kMask) {
 #pragma clang loop unroll(disable)
-  for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, lds_k0, lds_v1, lds_k1, lds_v0);
-    iteration(t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+    for (; t + 1 < n_tiles; t += 2) {
+      iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+      iteration(Fast{}, t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+    }
+    if (t < n_tiles) iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+  } else {
+    // head_dim 64: the tiles before the first one that needs the element mask
+    // (on the diagonal: keys before every row of the wavefront) run the
+    // interleaved block as long as the following tile needs no mask either;
+    // the rest the masked one.  Every wavefront runs n_tiles iterations with
+    // one barrier each, whichever block it takes.  (At head_dim 128 the two
+    // blocks in one kernel leave too few registers, and the masked block alone
+    // is faster.)
+    if constexpr (D == 64) {
+      const int first_diag = kDiag ? (q0w >= kBN - 1 ? (q0w - (kBN - 1)) / kBN + 1 : 0) : n_tiles;
+      const int first_tail = kv_rows >= kBN ? (kv_rows - kBN) / kBN + 1 : 0;
+      const int n_fast = max(0, min(min(first_diag, first_tail) - 1, n_tiles - 1));
+#pragma clang loop unroll(disable)
+      for (; t + 1 < n_fast; t += 2) {
+        iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+        iteration(Fast{}, t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+      }
+      if (t < n_fast) {
+        iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+        ++t;
+        if (t < n_tiles) iteration(Masked{}, t, lds_k1, lds_v0, lds_k0, lds_v1);
+        ++t;
+      }
+    }
+#pragma clang loop unroll(disable)
+    for (; t + 1 < n_tiles; t += 2) {
+      iteration(Masked{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+      iteration(Masked{}, t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+    }
+    if (t < n_tiles) iteration(Masked{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
   }
-  if (t < n_tiles) iteration(t, lds_k0, lds_v1, lds_k1, lds_v0);
 
   // ---- back to the canonical state (m = true running maximum) --------------
   const float l_tot = half_swap_sum(rs.l);
