@@ -275,7 +275,8 @@ def bench_backward(args, wl, rank):
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
     line = {
-        "metric": "causal bf16 ring-step attention backward TFLOP/s (c=4096, d=128)",
+        "metric": (f"{'causal' if wl.causal else 'non-causal'} {wl.dtype} ring-step attention backward "
+                   f"TFLOP/s (c={wl.rows}, d={wl.head_dim})"),
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,

@@ -197,11 +197,10 @@ ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t hea
  *   dk, dv    [batch, heads, rows, head_dim] fp32, accumulated (block j)
  *   q_block, kv_block, num_blocks, causal, scale   as in ra_step.
  * The caller zeroes the accumulators before a ring.  A skipped block returns
- * RA_OK and enqueues nothing.  bf16 inputs with head_dim 128 use the MFMA
- * path: two kernels (query-stationary for dq, key-stationary for dk and dv),
+ * RA_OK and enqueues nothing.  bf16 inputs use the MFMA path: two kernels (query-stationary for dq, key-stationary for dk and dv),
  * fp32 accumulation, P and dS rounded to bf16 before their products; each
  * output row is updated by one workgroup, so results are run-to-run
- * identical.  Other inputs use an fp32-arithmetic kernel that adds dk and dv
+ * identical.  fp32 inputs use an fp32-arithmetic kernel that adds dk and dv
  * with fp32 atomics (low bits may differ between runs).  bf16 blocks are
  * limited as in ra_step.
  */

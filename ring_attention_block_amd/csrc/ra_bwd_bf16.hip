@@ -1,4 +1,4 @@
-// Backward of one ring step for bf16 inputs with head_dim 128 on the CDNA4
+// Backward of one ring step for bf16 inputs (head_dim 64 or 128) on the CDNA4
 // matrix cores ("Ring Attention：把超长序列沿设备环流动", section "Backward
 // 需要让梯度也沿环传播": the query owner accumulates dQ, the dK and dV of the
 // visiting block accumulate while it travels; the probabilities are recomputed
@@ -24,14 +24,15 @@
 //
 // All products use v_mfma_f32_32x32x16_bf16 (lane l holds A[l%32][8(l/32)..]
 // and B[8(l/32)..][l%32]; accumulator entry i of lane l is D[8(i/4) + 4(l/32)
-// + i%4][l%32]).  Every streamed tile (64 rows x 128 bf16) has the same LDS
+// + i%4][l%32]).  Every streamed tile (64 rows x head_dim bf16) has the same LDS
 // layout:
 //  * physical row rho holds tile row kappa(rho), which swaps bits 2 and 3, so
 //    accumulator entries 8(i/8)..8(i/8)+7 of a product whose A operand is
 //    read row by row are 8 consecutive tile rows: they are directly the B
 //    operand (or, transposed, the A operand) of the next product;
 //  * the 16-byte chunks of each row are XOR-swizzled by
-//    f(rho) = sigma(rho & 3) ^ ((rho >> 2) & 3), sigma = {0, 6, 10, 12}, which
+//    f(rho) = sigma(rho & 3) ^ ((rho >> 2) & 3), sigma = {0, 6, 10, 12} at
+//    head_dim 128 (another f at 64, see swz), which
 //    keeps both access patterns free of bank conflicts: 16-byte reads of 16
 //    consecutive rows at one chunk (f is a permutation of 0..15 over them, and
 //    of 0..7 modulo 8 over each aligned 8), and the transposing reads
@@ -62,7 +63,7 @@ constexpr float kLog2e = 1.442695040888963407f;
 
 template <int D>
 struct BTile {
-  static_assert(D == 128, "the matrix-core backward is written for head_dim 128");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   static constexpr int kRowBytes = D * 2;
   static constexpr int kBytes = kBT * kRowBytes;
   static constexpr int kChunks = D / 8;
@@ -74,9 +75,17 @@ struct BTile {
 __device__ __forceinline__ int kappa(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
 }
+// 16-byte chunk swizzle of a tile row (see the layout notes above).  With
+// head_dim 64 a row has 8 chunks (128 bytes, two rows per 256 bytes of banks):
+// f(rho) = 2(rho & 3) ^ ((rho >> 2) & 3) is a permutation of 0..7 over every
+// aligned 8 rows and over the even and the odd rows of every aligned 16 (the
+// 16-byte reads), and over every aligned 4 rows f/2 takes four distinct values
+// with bit 2 differing between rows two apart (the transposing reads).
+template <int D>
 __device__ __forceinline__ int swz(int rho) {
   const int x = rho & 3;
-  return (4 * x + 2 * ((x ^ (x >> 1)) & 1)) ^ ((rho >> 2) & 3);
+  if constexpr (D == 128) return (4 * x + 2 * ((x ^ (x >> 1)) & 1)) ^ ((rho >> 2) & 3);
+  else return (2 * x) ^ ((rho >> 2) & 3);
 }
 
 // Workgroup -> (batch*head, tile): consecutive workgroup ids go to different
@@ -111,7 +120,7 @@ __device__ __forceinline__ void copy_offsets(uint32_t (&off)[BTile<D>::kLoadsPer
     const int n = wave + i * kWaves;
     const int rho = n * T::kRowsPerLoad + lane / T::kChunks;
     const int chi = lane % T::kChunks;
-    off[i] = (uint32_t)(kappa(rho) * T::kRowBytes + ((chi ^ swz(rho)) * 16));
+    off[i] = (uint32_t)(kappa(rho) * T::kRowBytes + ((chi ^ swz<D>(rho)) * 16));
   }
 }
 
@@ -168,14 +177,14 @@ __device__ __forceinline__ FragOffsets<D> frag_offsets(int lane) {
   const int r = lane & 31, h = lane >> 5, g = lane >> 4, j = lane & 15;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c)
-    fo.nrm[c] = (uint32_t)(r * T::kRowBytes + (((2 * c + h) ^ swz(r)) * 16));
+    fo.nrm[c] = (uint32_t)(r * T::kRowBytes + (((2 * c + h) ^ swz<D>(r)) * 16));
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int rho = 8 * e + 4 * h + (j >> 2);
       const int chunk = 4 * b + 2 * (g & 1) + ((j & 3) >> 1);
-      fo.tr[b][e] = (uint32_t)(rho * T::kRowBytes + ((chunk ^ swz(rho)) * 16) + 8 * (j & 1));
+      fo.tr[b][e] = (uint32_t)(rho * T::kRowBytes + ((chunk ^ swz<D>(rho)) * 16) + 8 * (j & 1));
     }
   return fo;
 }
@@ -344,7 +353,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
 // so query tiles are triple buffered: iteration u computes on tiles u and u+1
 // while tile u+2 is copied in.
 template <int D, bool kDiag>
-__global__ void __launch_bounds__(64 * kWaves, 1) bwd_dkdv_bf16_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = BTile<D>;
   constexpr int kBK = 32 * kWaves;
@@ -555,8 +564,10 @@ hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_step_bf16(const BwdArgs &a, int d, StepCase c, hipStream_t s) {
-  if (d != 128) return hipErrorInvalidValue;
-  return c == StepCase::Diag ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
+  const bool diag = c == StepCase::Diag;
+  if (d == 128) return diag ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
+  if (d == 64) return diag ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ra

@@ -260,7 +260,7 @@ ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_d
   a.scale_log2 = scale * 1.442695040888963407f;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
   (void)hipGetLastError();
-  const hipError_t e = (in_dtype == RA_BF16 && head_dim == 128)
+  const hipError_t e = in_dtype == RA_BF16
                           ? ra::launch_bwd_step_bf16(a, head_dim, sc, stream)
                           : ra::launch_bwd_step_simple(a, head_dim, in_dtype == RA_BF16, sc, stream);
   return hip_status(e, "ra_bwd_step launch");

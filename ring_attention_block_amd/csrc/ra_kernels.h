@@ -46,7 +46,7 @@ hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream
 hipError_t launch_bwd_prepare(const void *o, bool o_bf16, const void *dout, bool do_bf16,
                               float *delta, int64_t n_rows, int d, hipStream_t s);
 hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s);
-// Matrix-core backward step (bf16, head_dim 128 only).
+// Matrix-core backward step (bf16, head_dim 64 or 128).
 hipError_t launch_bwd_step_bf16(const BwdArgs &a, int d, StepCase c, hipStream_t s);
 
 }  // namespace ra

@@ -65,15 +65,18 @@ def _inputs(wl):
 
 
 SMALL = [
-    # (heads, head_dim, rows, blocks, dtype); bf16 with head_dim 128 runs the
-    # matrix-core kernels, the others the general kernel.
+    # (heads, head_dim, rows, blocks, dtype); bf16 runs the matrix-core
+    # kernels, fp32 the general kernel.
     (2, 128, 200, 3, "bf16"),
     (1, 64, 130, 3, "f32"),
     (8, 128, 640, 2, "bf16"),
     (16, 128, 1000, 2, "bf16"),
+    (4, 64, 300, 3, "bf16"),
+    (8, 64, 1000, 2, "bf16"),
     (2, 64, 96, 2, "bf16"),
     (1, 128, 64, 2, "f32"),
     (1, 128, 1, 2, "bf16"),
+    (1, 64, 7, 2, "bf16"),
 ]
 
 
@@ -116,7 +119,7 @@ def test_bwd_step_every_pair(heads, d, rows, P, dtype, causal):
             _say(f"  {what}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
 
 
-@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL[:4])
+@pytest.mark.parametrize("heads,d,rows,P,dtype", SMALL[:6])
 @pytest.mark.parametrize("causal", [True, False])
 def test_backward_ring_gives_full_gradients(heads, d, rows, P, dtype, causal):
     """Every rank's forward ring, then every rank's backward ring (dK, dV of
@@ -218,3 +221,50 @@ def test_bwd_prepare_row_dot(heads, d, rows, o_dtype, do_dtype):
     bound = np.sum(np.abs(oracle_values(d_h, wl_d) * oracle_values(o_h, wl_o)), axis=-1)
     err = np.abs(got[0].cpu().numpy().astype(np.float64) - want)
     assert np.all(err <= 1e-6 * d * bound + 1e-30), float(np.max(err / (bound + 1e-30)))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kv_block", [30, 31])
+def test_bwd_step_longshare_shape_sampled(kv_block):
+    """The step at the full size of the head_dim-64 workload (16 heads, 16384
+    rows per block, query block 31 of 32) against the oracle on sampled query
+    rows (dQ) and sampled keys (dK, dV) of two heads.  Those heads get the LSE
+    and D of attention over block kv_block alone, computed by the oracle; the
+    other heads an upper bound of each row's scaled scores as LSE and D = 0."""
+    wl = synth.WORKLOADS["longshare_bf16_h16_d64_c16384_p32"]
+    i, j, heads = 31, kv_block, (3, 12)
+    host = gen_blocks(wl, [(synth.ROLE_Q, i), (synth.ROLE_DO, i), (synth.ROLE_K, j), (synth.ROLE_V, j)])
+    dev = {key: to_device(x, wl) for key, x in host.items()}
+    f64 = {key: oracle_values(x, wl) for key, x in host.items()}
+    q, do = f64[(synth.ROLE_Q, i)], f64[(synth.ROLE_DO, i)]
+    k, v = f64[(synth.ROLE_K, j)], f64[(synth.ROLE_V, j)]
+    lse = (wl.scale * np.linalg.norm(q, axis=2) * np.linalg.norm(k, axis=2).max(axis=1)[:, None])
+    lse = lse.astype(np.float32)
+    delta = np.zeros_like(lse)
+    qpos, kpos = dense.ring_positions(i, wl.rows), dense.ring_positions(j, wl.rows)
+    for hd in heads:
+        o, l = dense.attention(q[hd:hd + 1], k[hd:hd + 1], v[hd:hd + 1], qpos, kpos, True, wl.scale)
+        lse[hd], delta[hd] = l[0], backward.row_dot(do[hd:hd + 1], o)[0]
+    shape = dev[(synth.ROLE_Q, i)].shape
+    dq, dk, dv = (torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(3))
+    _say(f"  bwd_step d64 shape i={i} j={j}")
+    _lib.bwd_step(dev[(synth.ROLE_Q, i)], dev[(synth.ROLE_DO, i)], torch.from_numpy(lse[None]).cuda(),
+                  torch.from_numpy(delta[None]).cuda(), dev[(synth.ROLE_K, j)], dev[(synth.ROLE_V, j)],
+                  dq, dk, dv, i, j, wl.blocks, True, wl.scale)
+    torch.cuda.synchronize()
+    for t, name in ((dq, "dQ"), (dk, "dK"), (dv, "dV")):
+        assert torch.isfinite(t).all(), f"{name}: non-finite values"
+    rows = synth.sample_rows(wl.seed, wl.rows, 96)
+    for hd in heads:
+        hs = slice(hd, hd + 1)
+        l64, d64 = lse[hs].astype(np.float64), delta[hs].astype(np.float64)
+        # dQ of the sampled rows: those rows against every key of the block.
+        wq, _, _ = backward.block_backward(q[hs][:, rows], k[hs], v[hs], do[hs][:, rows], l64[:, rows],
+                                           d64[:, rows], qpos[rows], kpos, True, wl.scale)
+        # dK, dV of the sampled keys: every query row against those keys.
+        _, wk, wv = backward.block_backward(q[hs], k[hs][:, rows], v[hs][:, rows], do[hs], l64, d64,
+                                            qpos, kpos[rows], True, wl.scale)
+        e = [_close(dq[0, hd, rows].cpu().numpy(), wq[0], wl, f"head {hd} dQ"),
+             _close(dk[0, hd, rows].cpu().numpy(), wk[0], wl, f"head {hd} dK"),
+             _close(dv[0, hd, rows].cpu().numpy(), wv[0], wl, f"head {hd} dV")]
+        _say(f"  j={j} head {hd}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
