@@ -268,3 +268,35 @@ def test_bwd_step_longshare_shape_sampled(kv_block):
              _close(dk[0, hd, rows].cpu().numpy(), wk[0], wl, f"head {hd} dK"),
              _close(dv[0, hd, rows].cpu().numpy(), wv[0], wl, f"head {hd} dV")]
         _say(f"  j={j} head {hd}: rel err dQ {e[0]:.1e} dK {e[1]:.1e} dV {e[2]:.1e}")
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "bf16"), (64, "f32")])
+def test_bwd_batch_is_an_outer_head_axis(d, dtype):
+    """ra_bwd_step with batch 2 on [2, H, rows, d] = the batch-1 call on 2H
+    heads, bit-identically for the matrix-core path (no atomics) and within
+    the tolerance for the general kernel (fp32 atomics)."""
+    heads, rows, P = 2, 200, 2
+    wl = synth.Workload(f"bwdbatch_{dtype}_d{d}", 800 + d, 2 * heads, d, rows, P, dtype, True, (1,))
+    _, dev, f64 = _inputs(wl)
+    o, lse = dense.attention(f64[(synth.ROLE_Q, 1)], np.concatenate([f64[(synth.ROLE_K, j)] for j in range(P)], 1),
+                             np.concatenate([f64[(synth.ROLE_V, j)] for j in range(P)], 1),
+                             dense.ring_positions(1, rows), np.arange(P * rows), True, wl.scale)
+    delta = backward.row_dot(f64[(synth.ROLE_DO, 1)], o)
+    out = []
+    for batch in (1, 2):
+        shape = (batch, 2 * heads // batch, rows, d)
+        v = lambda t: t.view(shape)
+        lse_d = torch.tensor(lse, dtype=torch.float32, device="cuda").view(shape[:3])
+        del_d = torch.tensor(delta, dtype=torch.float32, device="cuda").view(shape[:3])
+        g = [torch.zeros(shape, dtype=torch.float32, device="cuda") for _ in range(3)]
+        for j in range(P):
+            _lib.bwd_step(v(dev[(synth.ROLE_Q, 1)]), v(dev[(synth.ROLE_DO, 1)]), lse_d, del_d,
+                          v(dev[(synth.ROLE_K, j)]), v(dev[(synth.ROLE_V, j)]), g[0], g[1], g[2], 1, j, P,
+                          True, wl.scale)
+        torch.cuda.synchronize()
+        out.append([t.reshape(1, 2 * heads, rows, d) for t in g])
+    for a, b, name in zip(out[0], out[1], ("dQ", "dK", "dV")):
+        if dtype == "bf16":
+            assert torch.equal(a, b), name
+        else:
+            assert float((a - b).abs().max()) <= 1e-5 * float(a.abs().max()), name

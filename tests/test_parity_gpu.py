@@ -271,3 +271,27 @@ def test_million_token_rank_sampled_rows():
     rows = _rows_sample(C5, 256)
     _check(C5, o, lse, rank, True, rows=rows, cache=inp.cache,
            what=f"{len(rows)} rows x {C5.heads} heads")
+
+
+@pytest.mark.parametrize("d,rows,dtype", [(128, 300, "bf16"), (64, 200, "bf16"), (128, 130, "f32")])
+def test_batch_is_an_outer_head_axis(d, rows, dtype):
+    """[B, H, rows, d] with B = 2 is laid out as [1, 2H, rows, d]: a batch-2 ring
+    step must give bit-identical state to the batch-1 call on 2H heads, and
+    both match the oracle."""
+    heads, P, rank = 3, 3, 2
+    wl = synth.Workload(f"batch_{dtype}_d{d}_c{rows}", 700 + rows + d, 2 * heads, d, rows, P, dtype,
+                        True, (rank,))
+    inp = Inputs(wl, rank)
+    results = []
+    for batch in (1, 2):
+        shape = (batch, 2 * heads // batch, rows, d)
+        st = _lib.State(*shape)
+        emu = RingEmulator(shape, inp.q.dtype)
+        view = lambda t: t.view(shape)
+        emu.run(st, view(inp.q), lambda j: (view(inp.kv[j][0]), view(inp.kv[j][1])), rank, P, True,
+                wl.scale)
+        o, lse = _lib.finalize(st, torch.float32, emu.compute)
+        torch.cuda.synchronize()
+        results.append((o.reshape(1, 2 * heads, rows, d), lse.reshape(1, 2 * heads, rows)))
+    assert torch.equal(results[0][0], results[1][0]) and torch.equal(results[0][1], results[1][1])
+    _check(wl, results[1][0], results[1][1], rank, True, cache=inp.cache, what=f"batch 2 {wl.name}")
