@@ -224,6 +224,30 @@ __device__ __forceinline__ void add_row(float *dst, const f32x16 (&acc)[D / 32],
 }
 
 // ------------------------------------------------------------------ dQ ------
+// Instruction order of one 32-key half of a dQ tile (one scheduling region):
+// the fragment reads of the S/dP products issued eight ahead of the products
+// that use them, then the softmax, then the dQ products with their
+// transposing reads (two per product) issued four products ahead.  Without
+// it the compiler reuses one register quad for every fragment and each
+// product waits for its own read.  Masks: 0x008 MFMA, 0x100 LDS read, 0x402
+// VALU and transcendental.
+#define RA_DQ_INTERLEAVE(kQK_, kDB_)                                        \
+  do {                                                                      \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                      \
+    for (int i_ = 0; i_ < 2 * (kQK_) - 8; ++i_) {                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    \
+    }                                                                       \
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                      \
+    __builtin_amdgcn_sched_group_barrier(0x402, 200, 0);                    \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                      \
+    for (int i_ = 0; i_ < 2 * (kDB_) - 4; ++i_) {                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    \
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                    \
+    }                                                                       \
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                      \
+    __builtin_amdgcn_sched_barrier(0);                                      \
+  } while (0)
 template <int D, bool kDiag, bool kMask>
 __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -313,6 +337,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
         for (int b = 0; b < kDB; ++b)
           dq[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kb, fo, 2 * sb + half, b), dsb[half],
                                                           dq[b], 0, 0, 0);
+      if constexpr (!kMask) RA_DQ_INTERLEAVE(kQK, kDB);
     }
   };
   auto iteration = [&](int t, char *k_dst, char *v_dst, const char *k_src, const char *v_src) {
