@@ -44,6 +44,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ra_kernels.h"
 
 namespace ra {
@@ -56,6 +58,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) float4 lds_float4;
+
+using NoMask = std::integral_constant<bool, false>;
+using MayMask = std::integral_constant<bool, true>;
 
 constexpr int kBT = 64;        // rows per streamed tile
 constexpr int kWaves = 4;      // wavefronts per workgroup
@@ -310,8 +315,10 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
   const float sl2 = a.scale_log2;
   const int lim = kDiag ? min(row, rows - 1) : rows - 1;   // last key this row may see
 
-  auto body = [&](int t, const char *kb, const char *vb) {
-    const bool masked = kMask && ((kDiag && t * kBT + kBT - 1 > q0w) || (t * kBT + kBT > rows));
+  // may_mask (compile-time): the tile may need the element mask.
+  auto body = [&](auto may_mask, int t, const char *kb, const char *vb) {
+    constexpr bool kM = decltype(may_mask)::value;
+    const bool masked = kM && ((kDiag && t * kBT + kBT - 1 > q0w) || (t * kBT + kBT > rows));
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -337,15 +344,16 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
         for (int b = 0; b < kDB; ++b)
           dq[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_tr<D>(kb, fo, 2 * sb + half, b), dsb[half],
                                                           dq[b], 0, 0, 0);
-      if constexpr (!kMask) RA_DQ_INTERLEAVE(kQK, kDB);
+      if constexpr (!kM) RA_DQ_INTERLEAVE(kQK, kDB);
     }
   };
-  auto iteration = [&](int t, char *k_dst, char *v_dst, const char *k_src, const char *v_src) {
+  auto iteration = [&](auto may_mask, int t, char *k_dst, char *v_dst, const char *k_src,
+                       const char *v_src) {
     if (t + 1 < n_tiles) {
       issue_copy<D>(k_dst, rk, coff, (t + 1) * kBT, wave);
       issue_copy<D>(v_dst, rv, coff, (t + 1) * kBT, wave);
     }
-    if (!(kDiag && t * kBT > q0w + 31)) body(t, k_src, v_src);
+    if (!(kDiag && t * kBT > q0w + 31)) body(may_mask, t, k_src, v_src);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   };
@@ -353,12 +361,39 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int t = 0;
+  if constexpr (kMask) {
+    // The tiles before the first that needs the element mask for this
+    // wavefront (on the diagonal: keys before all of its rows; else the
+    // ragged last tile) run without it.  Every wavefront runs n_tiles
+    // iterations with one barrier each.
+    const int first_diag = kDiag ? (q0w >= kBT - 1 ? (q0w - (kBT - 1)) / kBT + 1 : 0) : n_tiles;
+    const int first_tail = rows >= kBT ? (rows - kBT) / kBT + 1 : 0;
+    const int n_fast = min(min(first_diag, first_tail), n_tiles);
 #pragma clang loop unroll(disable)
-  for (; t + 1 < n_tiles; t += 2) {
-    iteration(t, lds_k1, lds_v1, lds_k0, lds_v0);
-    iteration(t + 1, lds_k0, lds_v0, lds_k1, lds_v1);
+    for (; t + 1 < n_fast; t += 2) {
+      iteration(NoMask{}, t, lds_k1, lds_v1, lds_k0, lds_v0);
+      iteration(NoMask{}, t + 1, lds_k0, lds_v0, lds_k1, lds_v1);
+    }
+    if (t < n_fast) {
+      iteration(NoMask{}, t, lds_k1, lds_v1, lds_k0, lds_v0);
+      ++t;
+      if (t < n_tiles) iteration(MayMask{}, t, lds_k0, lds_v0, lds_k1, lds_v1);
+      ++t;
+    }
+#pragma clang loop unroll(disable)
+    for (; t + 1 < n_tiles; t += 2) {
+      iteration(MayMask{}, t, lds_k1, lds_v1, lds_k0, lds_v0);
+      iteration(MayMask{}, t + 1, lds_k0, lds_v0, lds_k1, lds_v1);
+    }
+    if (t < n_tiles) iteration(MayMask{}, t, lds_k1, lds_v1, lds_k0, lds_v0);
+  } else {
+#pragma clang loop unroll(disable)
+    for (; t + 1 < n_tiles; t += 2) {
+      iteration(NoMask{}, t, lds_k1, lds_v1, lds_k0, lds_v0);
+      iteration(NoMask{}, t + 1, lds_k0, lds_v0, lds_k1, lds_v1);
+    }
+    if (t < n_tiles) iteration(NoMask{}, t, lds_k1, lds_v1, lds_k0, lds_v0);
   }
-  if (t < n_tiles) iteration(t, lds_k1, lds_v1, lds_k0, lds_v0);
 
   if (row_ok) add_row<D>(a.dq + base + (size_t)row * D, dq, h, a.scale);
 #endif  // __HIP_DEVICE_COMPILE__
@@ -478,9 +513,10 @@ __global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_k
     }
   };
   // P and dS of a sub-tile as the B operands of the gradient products.
-  auto softmax = [&](const f32x16 &s, const f32x16 &dp, int buf, int t, int sb, bf16x8 (&pb)[2],
-                     bf16x8 (&dsb)[2]) {
-    const bool masked = needs_mask(t, sb);
+  // may_mask (compile-time): the sub-tile may cross the diagonal.
+  auto softmax = [&](auto may_mask, const f32x16 &s, const f32x16 &dp, int buf, int t, int sb,
+                     bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+    const bool masked = decltype(may_mask)::value && needs_mask(t, sb);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int q0 = sb * 32 + hh * 16 + 8 * h;
@@ -520,8 +556,12 @@ __global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_k
 
   // Iteration u: tile t = first + u in buffer bc, tile t+1 in b1, copies of
   // tile t+2 into b2.
-  auto iteration = [&](int u, int bc, int b1, int b2, const char *qc, const char *oc, const char *q1,
-                       const char *o1, char *q2, char *o2) {
+  // `generic` (compile-time): the tile may hold the diagonal of the
+  // workgroup's keys (masked and skipped sub-tiles); otherwise the pipelined
+  // block.
+  auto iteration = [&](auto generic, int u, int bc, int b1, int b2, const char *qc, const char *oc,
+                       const char *q1, const char *o1, char *q2, char *o2) {
+    constexpr bool kGeneric = decltype(generic)::value;
     const int t = first + u;
     float staged = 0.f;
     if (u + 2 < n) {
@@ -531,23 +571,23 @@ __global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_k
     }
     f32x16 s1, dp1;
     bf16x8 pb[2], dsb[2];
-    if (!kDiag) {
+    if constexpr (!kGeneric) {
       // First half: P, dS of (t, 0); S, dP of (t, 1); gradients of (t, 0).
-      softmax(s0, dp0, bc, t, 0, pb, dsb);
+      softmax(NoMask{}, s0, dp0, bc, t, 0, pb, dsb);
       sdp(qc, oc, 1, s1, dp1);
       grads(qc, oc, 0, pb, dsb);
       RA_DKDV_HALF_END();
       // Second half: P, dS of (t, 1); S, dP of (t+1, 0) (stale and unused
       // after the last tile); gradients of (t, 1).
-      softmax(s1, dp1, bc, t, 1, pb, dsb);
+      softmax(NoMask{}, s1, dp1, bc, t, 1, pb, dsb);
       sdp(q1, o1, 0, s0, dp0);
       grads(qc, oc, 1, pb, dsb);
       RA_DKDV_HALF_END();
     } else {
-      if (!skipped(t, 0)) softmax(s0, dp0, bc, t, 0, pb, dsb);
+      if (!skipped(t, 0)) softmax(MayMask{}, s0, dp0, bc, t, 0, pb, dsb);
       if (!skipped(t, 1)) sdp(qc, oc, 1, s1, dp1);
       if (!skipped(t, 0)) grads(qc, oc, 0, pb, dsb);
-      if (!skipped(t, 1)) softmax(s1, dp1, bc, t, 1, pb, dsb);
+      if (!skipped(t, 1)) softmax(MayMask{}, s1, dp1, bc, t, 1, pb, dsb);
       if (u + 1 < n && !skipped(t + 1, 0)) sdp(q1, o1, 0, s0, dp0);
       if (!skipped(t, 1)) grads(qc, oc, 1, pb, dsb);
     }
@@ -556,15 +596,34 @@ __global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_k
     __syncthreads();
   };
 
+  using Pipe = std::integral_constant<bool, false>;
+  using Generic = std::integral_constant<bool, true>;
   int u = 0;
+  if constexpr (!kDiag) {
 #pragma clang loop unroll(disable)
-  for (; u + 2 < n; u += 3) {
-    iteration(u, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
-    iteration(u + 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
-    iteration(u + 2, 2, 0, 1, lds_q2, lds_o2, lds_q0, lds_o0, lds_q1, lds_o1);
+    for (; u + 2 < n; u += 3) {
+      iteration(Pipe{}, u, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
+      iteration(Pipe{}, u + 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
+      iteration(Pipe{}, u + 2, 2, 0, 1, lds_q2, lds_o2, lds_q0, lds_o0, lds_q1, lds_o1);
+    }
+    if (u < n) iteration(Pipe{}, u, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
+    if (u + 1 < n) iteration(Pipe{}, u + 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
+  } else {
+    // The first two query tiles hold the diagonal of the workgroup's keys;
+    // every later query follows every key, so those tiles take the pipelined
+    // block (tile first+u stays in buffer u % 3).
+    iteration(Generic{}, 0, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
+    if (n > 1) iteration(Generic{}, 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
+    u = 2;
+#pragma clang loop unroll(disable)
+    for (; u + 2 < n; u += 3) {
+      iteration(Pipe{}, u, 2, 0, 1, lds_q2, lds_o2, lds_q0, lds_o0, lds_q1, lds_o1);
+      iteration(Pipe{}, u + 1, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
+      iteration(Pipe{}, u + 2, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
+    }
+    if (u < n) iteration(Pipe{}, u, 2, 0, 1, lds_q2, lds_o2, lds_q0, lds_o0, lds_q1, lds_o1);
+    if (u + 1 < n) iteration(Pipe{}, u + 1, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
   }
-  if (u < n) iteration(u, 0, 1, 2, lds_q0, lds_o0, lds_q1, lds_o1, lds_q2, lds_o2);
-  if (u + 1 < n) iteration(u + 1, 1, 2, 0, lds_q1, lds_o1, lds_q2, lds_o2, lds_q0, lds_o0);
 
   if (key_ok) {
     add_row<D>(a.dk + base + (size_t)key * D, dk, h, a.scale);
