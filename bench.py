@@ -2,12 +2,14 @@
 
 A "step" is one whole emulated ring of the rank: state init, the P ring steps
 (side-stream staging of the next key/value block, double-buffered swaps, one
-ra_step launch per non-skipped block) and the finalize.  Inputs are seeded
+ra_step launch per non-skipped block) and the finalize; by default the init
+and the finalize are fused into the first and the last launched step
+(ra_step_ex; --unfused launches them separately).  Inputs are seeded
 synthetic blocks already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--rank I]
                     [--partition contiguous|zigzag] [--decode-rows R] [--backward]
-                    [--no-cpu-baseline]
+                    [--unfused] [--no-cpu-baseline]
 
 Prints ONE JSON line.  FLOPs count 4*head_dim per unmasked (query, key) pair
 per head (the diagonal block counts c(c+1)/2 pairs, skipped blocks none).
@@ -315,6 +317,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward ring: the rank's backward ring (D, then the "
                          "P gradient steps with dK, dV travelling with the blocks)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate init and finalize launches instead of fusing them into the "
+                         "first and last ring steps (contiguous partition)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -366,9 +371,12 @@ def main():
         flops = ring_flops(wl, rank)
         baseline_q = rank
 
+        fused = not args.unfused
+
         def fold(timers, pool):
             emu.run(states[0], q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
-                    step_timers=timers, timer_events=pool)
+                    step_timers=timers, timer_events=pool,
+                    finalize_out=outs[0] if fused else None)
     else:
         # Zigzag: the sequence in 2P pieces of c/2 tokens; the rank holds
         # pieces (rank, 2P-1-rank), and each visit is up to four piece products.
@@ -392,6 +400,8 @@ def main():
                                               cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
         baseline_q = mine[1]
 
+        fused = False
+
         def fold(timers, pool):
             zz.run(states, qs, source, rank, wl.blocks, wl.causal, wl.scale,
                    step_timers=timers, timer_events=pool)
@@ -401,8 +411,9 @@ def main():
 
     def one_ring(timers=None, pool=None):
         fold(timers, pool)
-        for st, (o_out, lse_out) in zip(states, outs):
-            _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
+        if not fused:
+            for st, (o_out, lse_out) in zip(states, outs):
+                _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
 
     for _ in range(args.warmup):
         one_ring()
@@ -447,6 +458,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
         "config": {"workload": wl.name, "rank": rank, "partition": args.partition,
+                   "fused_init_finalize": fused,
                    "heads": wl.heads, "head_dim": wl.head_dim, "rows_per_block": wl.rows,
                    "blocks": wl.blocks, "causal": wl.causal, "tokens": wl.tokens,
                    "flop_per_step": flops,

@@ -58,6 +58,14 @@ typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 /* Result of the causal case test (ra_step_case). */
 typedef enum { RA_CASE_SKIP = 0, RA_CASE_DIAG = 1, RA_CASE_FULL = 2 } ra_case;
 
+/* Flags of ra_step_ex. */
+typedef enum {
+  RA_STEP_FRESH = 1,    /* the state is not read: the step starts from the empty
+                           state, as right after ra_state_init */
+  RA_STEP_FINALIZE = 2  /* the step writes ra_finalize's outputs instead of the
+                           state, which keeps its previous contents */
+} ra_step_flags;
+
 /*
  * Running online-softmax state of one rank's query block ("Ring Attention
  * Paper Breakdown ...", section 3: m, l in R^c and O in R^{c x d} per head,
@@ -125,6 +133,28 @@ int32_t ra_step_case(int32_t q_block, int32_t kv_block, int32_t num_blocks, int3
 ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
                   int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
                   int32_t causal, float scale, hipStream_t stream);
+
+/*
+ * ra_step with the first and the last fold of a ring fused with ra_state_init
+ * and ra_finalize (the normalisation of the pages' last step, RAMD section
+ * "Accumulation math, step by step": out = O / l; the saved LSE of the
+ * backward section of "Ring Attention：把超长序列沿设备环流动"), so a ring needs
+ * no separate init and finalize launches.  Arguments as in ra_step, plus:
+ *   flags      0, RA_STEP_FRESH, RA_STEP_FINALIZE or both (else
+ *              RA_ERR_INVALID_ARG).  RA_STEP_FRESH: m, l and o are not read;
+ *              the result is that of ra_state_init followed by ra_step.
+ *              RA_STEP_FINALIZE: instead of storing the new state the step
+ *              writes o_out and lse_out exactly as ra_finalize would from it
+ *              (bit-identical); m, l and o keep their previous contents.
+ *   o_out, out_dtype, lse_out   as in ra_finalize (used with
+ *              RA_STEP_FINALIZE only; either may be NULL; 16-byte aligned).
+ * A step that folds nothing (a skipped causal block, kv_rows == 0) still
+ * applies its flags, by enqueueing ra_state_init and ra_finalize.
+ */
+ra_status ra_step_ex(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
+                     int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                     int32_t causal, float scale, uint32_t flags, void *o_out, ra_dtype out_dtype,
+                     float *lse_out, hipStream_t stream);
 
 /*
  * dst <- dst (+) src: merge two partial states over disjoint key sets

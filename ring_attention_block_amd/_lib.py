@@ -19,7 +19,7 @@ RA_F32, RA_BF16 = 0, 1
 RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
 
 # Every symbol include/ra.h declares.
-EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_lse_merge", "ra_finalize",
+EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_lse_merge", "ra_finalize",
            "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_status_string", "ra_last_error")
 
 
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
             "ra_state_init": (ctypes.c_int, [sp, vp]),
             "ra_step_case": (i32, [i32, i32, i32, i32]),
             "ra_step": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp]),
+            "ra_step_ex": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32,
+                                          ctypes.c_uint32, vp, ctypes.c_int, vp, vp]),
             "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
             "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
@@ -129,9 +131,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
+RA_STEP_FRESH, RA_STEP_FINALIZE = 1, 2
+
+
 def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
-         scale: float, stream=None) -> int:
-    """Fold block kv_block into st; returns the causal case (0 skip, 1 diag, 2 full)."""
+         scale: float, stream=None, flags: int = 0, o_out=None, lse_out=None) -> int:
+    """Fold block kv_block into st; returns the causal case (0 skip, 1 diag, 2 full).
+
+    flags (ra_step_ex): RA_STEP_FRESH starts from the empty state without
+    reading st; RA_STEP_FINALIZE writes o_out (fp32 or bf16) and lse_out
+    instead of st, as finalize would.
+    """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
@@ -142,9 +152,22 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
         raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if tuple(q.shape) != st.shape:
         raise ValueError(f"q shape {tuple(q.shape)} does not match the state {st.shape}")
-    _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
-                         k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
-                         _stream(stream)))
+    if flags == 0:
+        _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                             k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
+                             _stream(stream)))
+    else:
+        b, h, r, d = st.shape
+        if o_out is not None and (tuple(o_out.shape) != (b, h, r, d) or not o_out.is_contiguous()
+                                  or o_out.dtype not in (torch.float32, torch.bfloat16)):
+            raise ValueError("o_out must be a contiguous fp32 or bf16 tensor of the state's shape")
+        if lse_out is not None and (tuple(lse_out.shape) != (b, h, r) or not lse_out.is_contiguous()
+                                    or lse_out.dtype != torch.float32):
+            raise ValueError("lse_out must be a contiguous fp32 [B,H,rows] tensor")
+        out_code = RA_BF16 if o_out is not None and o_out.dtype == torch.bfloat16 else RA_F32
+        _check(lib().ra_step_ex(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                                k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
+                                int(flags), _ptr(o_out), out_code, _ptr(lse_out), _stream(stream)))
     return step_case(q_block, kv_block, num_blocks, causal)
 
 

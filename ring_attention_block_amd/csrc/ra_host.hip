@@ -117,37 +117,58 @@ ra_status ra_state_init(ra_state *st, hipStream_t stream) {
                     "ra_state_init launch");
 }
 
-ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
-                  int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
-                  int32_t causal, float scale, hipStream_t stream) {
+namespace {
+
+// ra_step and ra_step_ex: every check before anything is enqueued.
+ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k, const void *v,
+                    ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
+                    int32_t num_blocks, int32_t causal, float scale, uint32_t flags, void *o_out,
+                    ra_dtype out_dtype, float *lse_out, hipStream_t stream) {
   int64_t n = 0;
-  ra_status s = check_state(st, "ra_step", &n);
+  ra_status s = check_state(st, name, &n);
   if (s != RA_OK) return s;
   const int32_t c = ra_step_case(q_block, kv_block, num_blocks, causal);
   if (c < 0) return (ra_status)c;
   if (in_dtype != RA_F32 && in_dtype != RA_BF16)
-    return fail(RA_ERR_INVALID_ARG, "ra_step: in_dtype=%d is not RA_F32 or RA_BF16", (int)in_dtype);
-  if (kv_rows < 0) return fail(RA_ERR_INVALID_ARG, "ra_step: kv_rows=%d is negative", kv_rows);
+    return fail(RA_ERR_INVALID_ARG, "%s: in_dtype=%d is not RA_F32 or RA_BF16", name, (int)in_dtype);
+  if (kv_rows < 0) return fail(RA_ERR_INVALID_ARG, "%s: kv_rows=%d is negative", name, kv_rows);
   if (kv_rows != st->rows && causal)
     return fail(RA_ERR_UNSUPPORTED,
-                "ra_step: kv_rows=%d differs from rows=%d under the causal mask (equal blocks only)",
+                "%s: kv_rows=%d differs from rows=%d under the causal mask (equal blocks only)", name,
                 kv_rows, st->rows);
   if ((int64_t)st->batch * st->heads * kv_rows > ((int64_t)1 << 40) / st->head_dim)
-    return fail(RA_ERR_INVALID_ARG, "ra_step: key/value block of %d rows is too large", kv_rows);
+    return fail(RA_ERR_INVALID_ARG, "%s: key/value block of %d rows is too large", name, kv_rows);
   if (in_dtype == RA_BF16 && bf16_block_too_long(st->rows > kv_rows ? st->rows : kv_rows, st->head_dim))
-    return fail(RA_ERR_UNSUPPORTED, "ra_step: bf16 blocks are limited to 2^31 bytes per (batch, head)");
+    return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks are limited to 2^31 bytes per (batch, head)", name);
   if (!(scale > 0.f) || !isfinite(scale))
-    return fail(RA_ERR_INVALID_ARG, "ra_step: scale=%g must be finite and > 0", (double)scale);
+    return fail(RA_ERR_INVALID_ARG, "%s: scale=%g must be finite and > 0", name, (double)scale);
+  if (flags & ~(uint32_t)(RA_STEP_FRESH | RA_STEP_FINALIZE))
+    return fail(RA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, (unsigned)flags);
+  if (flags & RA_STEP_FINALIZE) {
+    if (out_dtype != RA_F32 && out_dtype != RA_BF16)
+      return fail(RA_ERR_INVALID_ARG, "%s: out_dtype=%d is not RA_F32 or RA_BF16", name, (int)out_dtype);
+    if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
+      return fail(RA_ERR_INVALID_ARG, "%s: outputs must be 16-byte aligned", name);
+  }
   if (n > 0) {
-    if (!q) return fail(RA_ERR_INVALID_ARG, "ra_step: NULL q");
-    if (!aligned16(q)) return fail(RA_ERR_INVALID_ARG, "ra_step: q must be 16-byte aligned");
+    if (!q) return fail(RA_ERR_INVALID_ARG, "%s: NULL q", name);
+    if (!aligned16(q)) return fail(RA_ERR_INVALID_ARG, "%s: q must be 16-byte aligned", name);
     if (kv_rows > 0) {
-      if (!k || !v) return fail(RA_ERR_INVALID_ARG, "ra_step: NULL k or v");
+      if (!k || !v) return fail(RA_ERR_INVALID_ARG, "%s: NULL k or v", name);
       if (!aligned16(k) || !aligned16(v))
-        return fail(RA_ERR_INVALID_ARG, "ra_step: k and v must be 16-byte aligned");
+        return fail(RA_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", name);
     }
   }
-  if (c == RA_CASE_SKIP || n == 0 || kv_rows == 0) return ok();  // nothing to fold
+  if (n == 0) return ok();
+  if (c == RA_CASE_SKIP || kv_rows == 0) {
+    // Nothing to fold: the flags still take effect through the state kernels.
+    if (flags & RA_STEP_FRESH) {
+      s = ra_state_init(st, stream);
+      if (s != RA_OK) return s;
+    }
+    if (flags & RA_STEP_FINALIZE) return ra_finalize(st, o_out, out_dtype, lse_out, stream);
+    return ok();
+  }
 
   ra::StepArgs a;
   a.q = q;
@@ -160,11 +181,32 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
   a.kv_rows = kv_rows;
   a.bh = st->batch * st->heads;
   a.scale_log2 = scale * 1.442695040888963407f;
+  a.flags = (flags & RA_STEP_FRESH ? ra::kStepFresh : 0u) | (flags & RA_STEP_FINALIZE ? ra::kStepFinalize : 0u);
+  a.o_out = (flags & RA_STEP_FINALIZE) ? o_out : nullptr;
+  a.lse_out = (flags & RA_STEP_FINALIZE) ? lse_out : nullptr;
+  a.out_bf16 = out_dtype == RA_BF16;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
   (void)hipGetLastError();
   const hipError_t e = in_dtype == RA_BF16 ? ra::launch_step_bf16(a, st->head_dim, sc, stream)
                                            : ra::launch_step_f32(a, st->head_dim, sc, stream);
-  return hip_status(e, "ra_step launch");
+  return hip_status(e, name);
+}
+
+}  // namespace
+
+ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
+                  int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                  int32_t causal, float scale, hipStream_t stream) {
+  return step_impl("ra_step", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks, causal,
+                   scale, 0u, nullptr, RA_F32, nullptr, stream);
+}
+
+ra_status ra_step_ex(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
+                     int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                     int32_t causal, float scale, uint32_t flags, void *o_out, ra_dtype out_dtype,
+                     float *lse_out, hipStream_t stream) {
+  return step_impl("ra_step_ex", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks,
+                   causal, scale, flags, o_out, out_dtype, lse_out, stream);
 }
 
 ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream) {

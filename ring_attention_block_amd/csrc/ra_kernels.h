@@ -16,7 +16,19 @@ struct StepArgs {
   int32_t kv_rows;        // key/value rows of the visiting block (== rows for a diagonal block)
   int32_t bh;             // batch * heads
   float scale_log2;       // score scale * log2(e): kernels work in base 2
+  uint32_t flags;         // kStepFresh, kStepFinalize
+  void *o_out;            // kStepFinalize: O / l ([bh, rows, D], fp32 or bf16), may be NULL
+  float *lse_out;         // kStepFinalize: m + ln l ([bh, rows]), may be NULL
+  int32_t out_bf16;       // kStepFinalize: o_out is bf16
 };
+
+// The state is not read: the step starts from the empty state (m = -inf,
+// l = 0, O = 0), as after state init.
+constexpr uint32_t kStepFresh = 1u;
+// The step writes the finalized O / l and LSE = m + ln l (exactly as the
+// finalize kernel would from the state it would have stored) instead of the
+// state, which keeps its previous contents.
+constexpr uint32_t kStepFinalize = 2u;
 
 enum class StepCase : int { Diag = 1, Full = 2 };
 

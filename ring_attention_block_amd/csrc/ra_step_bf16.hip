@@ -326,10 +326,11 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       qf[c] = __builtin_bit_cast(bf16x8, u);
     }
     const size_t sr = (size_t)bh * rows + row;
-    const float m_state = row_ok ? a.m[sr] * kLog2e : -INFINITY;
+    const bool read_state = row_ok && !(a.flags & kStepFresh);
+    const float m_state = read_state ? a.m[sr] * kLog2e : -INFINITY;
     rs.m_ref = m_state;
     rs.m_run = m_state;
-    rs.l = (row_ok && h == 0) ? a.l[sr] : 0.f;
+    rs.l = (read_state && h == 0) ? a.l[sr] : 0.f;
   }
 
   // Per-lane LDS byte offsets of the fragments within a tile buffer.
@@ -403,11 +404,12 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // them and they overlap the first scores.
   {
     const size_t ro = (size_t)row * D;
+    const bool read_o = row_ok && !(a.flags & kStepFresh);
 #pragma unroll
     for (int b = 0; b < kDB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float4 x = row_ok ? *reinterpret_cast<const float4 *>(O + ro + b * 32 + g * 8 + h * 4)
+        float4 x = read_o ? *reinterpret_cast<const float4 *>(O + ro + b * 32 + g * 8 + h * 4)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
         oacc[b][4 * g + 0] = x.x;
         oacc[b][4 * g + 1] = x.y;
@@ -537,7 +539,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // ---- back to the canonical state (m = true running maximum) --------------
   const float l_tot = half_swap_sum(rs.l);
   const float beta = (rs.m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(rs.m_ref - rs.m_run);
-  if (row_ok) {
+  if (row_ok && !(a.flags & kStepFinalize)) {
     const size_t ro = (size_t)row * D;
 #pragma unroll
     for (int b = 0; b < kDB; ++b)
@@ -551,6 +553,36 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       const size_t sr = (size_t)bh * rows + row;
       a.m[sr] = rs.m_run * kLn2;
       a.l[sr] = l_tot * beta;
+    }
+  } else if (row_ok) {
+    // Finalize in place of the store: out = O / l and LSE = m + ln l of the
+    // state the branch above would store (l == 0 gives 0 and -inf).
+    const float lr = l_tot * beta;
+    const size_t oe = base + (size_t)row * D;
+    if (a.o_out) {
+#pragma unroll
+      for (int b = 0; b < kDB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = lr > 0.f ? (oacc[b][4 * g + e] * beta) / lr : 0.f;
+          const size_t at = oe + b * 32 + g * 8 + h * 4;
+          if (a.out_bf16) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 pk = {(__bf16)y[0], (__bf16)y[1], (__bf16)y[2], (__bf16)y[3]};
+            *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(a.o_out) + at) = pk;
+          } else {
+            *reinterpret_cast<float4 *>(static_cast<float *>(a.o_out) + at) =
+                make_float4(y[0], y[1], y[2], y[3]);
+          }
+        }
+    }
+    if (h == 0 && a.lse_out) {
+      // m is rounded to fp32 before the add, as the stored state is.
+#pragma clang fp contract(off)
+      const float m_nat = rs.m_run * kLn2;
+      a.lse_out[(size_t)bh * rows + row] = lr > 0.f ? m_nat + logf(lr) : -INFINITY;
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__

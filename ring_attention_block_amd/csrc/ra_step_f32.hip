@@ -43,14 +43,15 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
   float *__restrict__ O = a.o + base;
   const size_t srow = (size_t)bh * rows + row;
 
+  const bool read_state = row_ok && !(a.flags & kStepFresh);
   float qv[kPart], ov[kPart];
 #pragma unroll
   for (int x = 0; x < kPart; ++x) {
     qv[x] = row_ok ? Q[(size_t)row * D + part * kPart + x] : 0.f;
-    ov[x] = row_ok ? O[(size_t)row * D + part * kPart + x] : 0.f;
+    ov[x] = read_state ? O[(size_t)row * D + part * kPart + x] : 0.f;
   }
-  float m2 = row_ok ? a.m[srow] * kLog2e : -INFINITY;  // base-2 running max
-  float l = row_ok ? a.l[srow] : 0.f;
+  float m2 = read_state ? a.m[srow] * kLog2e : -INFINITY;  // base-2 running max
+  float l = read_state ? a.l[srow] : 0.f;
 
   const int kv_end = kDiag ? min(kv_rows, (qt + 1) * kRows) : kv_rows;
   for (int k0 = 0; k0 < kv_end; k0 += kKeys) {
@@ -94,12 +95,33 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
     m2 = mn;
   }
 
-  if (row_ok) {
+  if (row_ok && !(a.flags & kStepFinalize)) {
 #pragma unroll
     for (int x = 0; x < kPart; ++x) O[(size_t)row * D + part * kPart + x] = ov[x];
     if (part == 0) {
       a.m[srow] = m2 * kLn2;
       a.l[srow] = l;
+    }
+  } else if (row_ok) {
+    // Finalize in place of the store (as the finalize kernel would).
+    const size_t oe = base + (size_t)row * D + part * kPart;
+    if (a.o_out) {
+#pragma unroll
+      for (int x = 0; x < kPart; ++x) {
+        const float y = l > 0.f ? ov[x] / l : 0.f;
+        if (a.out_bf16) {
+          const __bf16 hb = (__bf16)y;
+          static_cast<uint16_t *>(a.o_out)[oe + x] = __builtin_bit_cast(uint16_t, hb);
+        } else {
+          static_cast<float *>(a.o_out)[oe + x] = y;
+        }
+      }
+    }
+    if (part == 0 && a.lse_out) {
+      // m is rounded to fp32 before the add, as the stored state is.
+#pragma clang fp contract(off)
+      const float m_nat = m2 * kLn2;
+      a.lse_out[srow] = l > 0.f ? m_nat + logf(l) : -INFINITY;
     }
   }
 }

@@ -126,26 +126,27 @@ class RingEmulator:
             self.ev_start.wait(comp)
 
     def step(self, st, q, k, v, i, j, num_blocks, causal, scale, case, step_timers=None,
-             timer_events=None) -> None:
-        """One ra_step on the compute stream, bracketed by timing events when
-        step_timers is given (see run)."""
+             timer_events=None, flags=0, out=(None, None)) -> None:
+        """One ra_step (ra_step_ex with flags) on the compute stream, bracketed
+        by timing events when step_timers is given (see run)."""
         comp = self.compute
+        kw = dict(flags=flags, o_out=out[0], lse_out=out[1])
         if step_timers is not None and case != _lib.RA_CASE_SKIP:
             if timer_events is not None:
                 e0, e1 = next(timer_events), next(timer_events)
             else:
                 e0, e1 = Event(timing=True), Event(timing=True)
             e0.record(comp)
-            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp)
+            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp, **kw)
             e1.record(comp)
             step_timers.append((case, e0, e1))
         else:
-            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp)
+            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp, **kw)
 
     def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
             rank: int, num_blocks: int, causal: bool, scale: float,
             order: Sequence[int] | None = None, init: bool = True,
-            step_timers: list | None = None, timer_events=None) -> list:
+            step_timers: list | None = None, timer_events=None, finalize_out=None) -> list:
         """Contiguous partition: fold the blocks of `order` (default: the ring
         order of `rank`) into st.
 
@@ -154,20 +155,35 @@ class RingEmulator:
         launched step, recorded on the compute stream around the launch;
         timer_events, if given, is an iterator of timing events created
         beforehand (two per launched step), so that no event is created while
-        work is being enqueued.  Returns the causal case of each step.
+        work is being enqueued.
+        finalize_out = (o_out, lse_out), if given, fuses the ring's init and
+        finalize into its first and last launched steps (ra_step_ex): the
+        first starts from the empty state (when init), the last writes
+        o_out, lse_out as finalize would, instead of the state.
+        Returns the causal case of each step.
         """
         order = ring_order(rank, num_blocks) if order is None else list(order)
-        if init:
+        all_cases = [_lib.step_case(rank, j, num_blocks, causal) for j in order]
+        launched = [s for s, c in enumerate(all_cases) if c != _lib.RA_CASE_SKIP]
+        fuse = finalize_out is not None and len(launched) > 0
+        if init and not fuse:
             _lib.state_init(st, self.compute)
         cases = []
 
         def fold(s, j, kv):
-            case = _lib.step_case(rank, j, num_blocks, causal)
+            case = all_cases[s]
+            flags = 0
+            if fuse and init and s == launched[0]:
+                flags |= _lib.RA_STEP_FRESH
+            if fuse and s == launched[-1]:
+                flags |= _lib.RA_STEP_FINALIZE
             self.step(st, q, kv[0], kv[1], rank, j, num_blocks, causal, scale, case,
-                      step_timers, timer_events)
+                      step_timers, timer_events, flags, finalize_out if flags else (None, None))
             cases.append(case)
 
         self.visit(order, kv_source, fold)
+        if finalize_out is not None and not fuse:
+            _lib.finalize(st, stream=self.compute, o_out=finalize_out[0], lse_out=finalize_out[1])
         return cases
 
 

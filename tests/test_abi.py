@@ -165,3 +165,21 @@ def test_bwd_rejects_before_enqueue(L):
         assert prep(**{name: 0}) == _lib.RA_ERR_INVALID_ARG, name
         assert prep(**{name: FAKE + 8}) == _lib.RA_ERR_INVALID_ARG, name
     assert prep(rows=0, o=0, dout=0, delta=0) == _lib.RA_OK
+
+
+def test_step_ex_rejects_before_enqueue(L):
+    st = _state()
+    def ex(flags, o=FAKE, ot=_lib.RA_F32, lse=FAKE, **kw):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, i=1, j=0, P=2, causal=1)
+        args.update(kw)
+        return L.ra_step_ex(ctypes.byref(st), args["q"], args["k"], args["v"], _lib.RA_BF16, st.rows,
+                            args["i"], args["j"], args["P"], args["causal"], 0.125, flags, o, ot, lse, None)
+    assert ex(4) == _lib.RA_ERR_INVALID_ARG
+    assert b"ra_step_ex" in L.ra_last_error() and b"flags" in L.ra_last_error()
+    assert ex(_lib.RA_STEP_FINALIZE, ot=3) == _lib.RA_ERR_INVALID_ARG
+    assert ex(_lib.RA_STEP_FINALIZE, o=FAKE + 8) == _lib.RA_ERR_INVALID_ARG
+    assert ex(_lib.RA_STEP_FINALIZE, lse=FAKE + 4) == _lib.RA_ERR_INVALID_ARG
+    assert ex(_lib.RA_STEP_FRESH, q=0) == _lib.RA_ERR_INVALID_ARG
+    assert ex(3, i=2) == _lib.RA_ERR_INVALID_ARG
+    # flags 0 on a skipped block: nothing enqueued, as ra_step
+    assert ex(0, i=0, j=1) == _lib.RA_OK

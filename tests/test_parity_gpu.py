@@ -295,3 +295,55 @@ def test_batch_is_an_outer_head_axis(d, rows, dtype):
         results.append((o.reshape(1, 2 * heads, rows, d), lse.reshape(1, 2 * heads, rows)))
     assert torch.equal(results[0][0], results[1][0]) and torch.equal(results[0][1], results[1][1])
     _check(wl, results[1][0], results[1][1], rank, True, cache=inp.cache, what=f"batch 2 {wl.name}")
+
+
+FUSED = [(2, 128, 300, 3, "bf16"), (1, 64, 200, 4, "f32"), (3, 64, 129, 2, "bf16")]
+
+
+@pytest.mark.parametrize("heads,d,rows,P,dtype", FUSED)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_fused_init_finalize_ring_is_bit_identical(heads, d, rows, P, dtype, causal, out_dtype):
+    """ra_step_ex: the ring with init fused into its first step (state not read:
+    it is filled with NaN first) and finalize into its last gives exactly the
+    outputs of the ring with separate ra_state_init and ra_finalize."""
+    wl = synth.Workload(f"fused_{dtype}_h{heads}_d{d}_c{rows}_p{P}", 900 + rows + d, heads, d, rows,
+                        P, dtype, causal, tuple(range(P)))
+    inp = Inputs(wl, 0)
+    for rank in range(P):
+        inp.set_rank(rank)
+        st = _lib.State(1, heads, rows, d)
+        emu = RingEmulator(inp.q.shape, inp.q.dtype)
+        emu.run(st, inp.q, lambda j: inp.kv[j], rank, P, causal, wl.scale)
+        want = _lib.finalize(st, out_dtype, emu.compute)
+        for t in (st.m, st.l, st.o):
+            t.fill_(float("nan"))
+        o = torch.empty(want[0].shape, dtype=out_dtype, device="cuda")
+        lse = torch.empty(want[1].shape, dtype=torch.float32, device="cuda")
+        emu.run(st, inp.q, lambda j: inp.kv[j], rank, P, causal, wl.scale, finalize_out=(o, lse))
+        torch.cuda.synchronize()
+        assert torch.equal(o, want[0]) and torch.equal(lse, want[1]), (rank, causal)
+        if out_dtype == torch.float32:
+            _check(wl, o, lse, rank, causal, cache=inp.cache, what=f"fused {wl.name} rank {rank}")
+
+
+def test_step_ex_finalize_leaves_state_and_skip_applies_flags():
+    wl = synth.Workload("stepex_bf16", 950, 2, 128, 192, 2, "bf16", True, (0, 1))
+    inp = Inputs(wl, 1)
+    st = _lib.State(1, 2, 192, 128)
+    _lib.state_init(st)
+    _lib.step(st, inp.q, *inp.kv[1], 1, 1, 2, True, wl.scale)
+    before = [t.clone() for t in (st.m, st.l, st.o)]
+    o = torch.empty(st.o.shape, dtype=torch.float32, device="cuda")
+    lse = torch.empty(st.m.shape, dtype=torch.float32, device="cuda")
+    _lib.step(st, inp.q, *inp.kv[0], 1, 0, 2, True, wl.scale, flags=_lib.RA_STEP_FINALIZE,
+              o_out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, (st.m, st.l, st.o)))
+    _check(wl, o, lse, 1, True, cache=inp.cache, what="finalizing step")
+    # A skipped block still applies both flags: empty state, O = 0, LSE = -inf.
+    case = _lib.step(st, inp.q, *inp.kv[1], 0, 1, 2, True, wl.scale,
+                     flags=_lib.RA_STEP_FRESH | _lib.RA_STEP_FINALIZE, o_out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    assert case == _lib.RA_CASE_SKIP
+    assert not o.any() and bool(torch.isneginf(lse).all()) and bool(torch.isneginf(st.m).all())
