@@ -319,7 +319,7 @@ def main():
                          "P gradient steps with dK, dV travelling with the blocks)")
     ap.add_argument("--unfused", action="store_true",
                     help="separate init and finalize launches instead of fusing them into the "
-                         "first and last ring steps (contiguous partition)")
+                         "first and last ring steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -400,11 +400,11 @@ def main():
                                               cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
         baseline_q = mine[1]
 
-        fused = False
+        fused = not args.unfused
 
         def fold(timers, pool):
             zz.run(states, qs, source, rank, wl.blocks, wl.causal, wl.scale,
-                   step_timers=timers, timer_events=pool)
+                   step_timers=timers, timer_events=pool, finalize_outs=outs if fused else None)
 
     outs = [(torch.empty(st.o.shape, dtype=torch.float32, device=dev),
              torch.empty(st.m.shape, dtype=torch.float32, device=dev)) for st in states]

@@ -63,8 +63,8 @@ class ShardedDecode:
         for p, (k, v) in enumerate(kv):
             s = self.streams[p]
             self.ev_start.wait(s)
-            _lib.state_init(self.states[p], s)
-            _lib.step(self.states[p], q, k, v, 0, 0, 1, False, scale, s)
+            # The local fold starts from the empty state (init fused into the step).
+            _lib.step(self.states[p], q, k, v, 0, 0, 1, False, scale, s, flags=_lib.RA_STEP_FRESH)
             self.ev_done[p].record(s)
         for p in range(self.shards):
             self.ev_done[p].wait(self.compute)

@@ -249,22 +249,40 @@ class ZigzagRing:
     def run(self, states: Sequence[_lib.State], qs: Sequence[torch.Tensor],
             kv_source: Callable[[int], tuple], rank: int, ranks: int, causal: bool,
             scale: float, init: bool = True, step_timers: list | None = None,
-            timer_events=None) -> list:
+            timer_events=None, finalize_outs=None) -> list:
         """Fold every visiting rank's two sub-blocks into the two states.
-        Returns zigzag_plan(rank, ranks, causal)."""
+        finalize_outs = [(o_out, lse_out)] * 2, if given, fuses each state's
+        init and finalize into its first and last launched piece product, as
+        RingEmulator.run does.  Returns zigzag_plan(rank, ranks, causal)."""
         plan = zigzag_plan(rank, ranks, causal)
-        if init:
-            for st in states:
-                _lib.state_init(st, self.compute)
         mine = zigzag_blocks(rank, ranks)
+        prods = [(s, a, b) for s, (_, ps) in enumerate(plan) for a, b, c in ps
+                 if c != _lib.RA_CASE_SKIP]
+        firsts = {a: next((p for p in prods if p[1] == a), None) for a in range(2)}
+        lasts = {a: next((p for p in reversed(prods) if p[1] == a), None) for a in range(2)}
+        fuse = [finalize_outs is not None and firsts[a] is not None for a in range(2)]
+        for a, st in enumerate(states):
+            if init and not fuse[a]:
+                _lib.state_init(st, self.compute)
 
         def fold(s, j, kv):
             theirs = zigzag_blocks(j, ranks)
             for a, b, case in plan[s][1]:
+                flags = 0
+                if fuse[a] and init and (s, a, b) == firsts[a]:
+                    flags |= _lib.RA_STEP_FRESH
+                if fuse[a] and (s, a, b) == lasts[a]:
+                    flags |= _lib.RA_STEP_FINALIZE
                 self.emu.step(states[a], qs[a], kv[b], kv[2 + b], mine[a], theirs[b],
-                              2 * ranks, causal, scale, case, step_timers, timer_events)
+                              2 * ranks, causal, scale, case, step_timers, timer_events, flags,
+                              finalize_outs[a] if flags else (None, None))
 
         self.emu.visit([j for j, _ in plan], kv_source, fold)
+        if finalize_outs is not None:
+            for a, st in enumerate(states):
+                if not fuse[a]:
+                    _lib.finalize(st, stream=self.compute, o_out=finalize_outs[a][0],
+                                  lse_out=finalize_outs[a][1])
         return plan
 
     def run_backward(self, qs: Sequence[torch.Tensor], douts: Sequence[torch.Tensor],

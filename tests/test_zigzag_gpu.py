@@ -160,3 +160,37 @@ def test_zigzag_backward_all_ranks(heads, d, rows, P, dtype, causal):
             err = float(np.max(np.abs(g - w)))
             assert np.isfinite(g).all() and err <= rel * scale_, (b, name, err, scale_)
         _say(f"  {sub.name} causal={causal} piece {b} ok")
+
+
+@pytest.mark.parametrize("heads,d,rows,P,dtype", [(2, 128, 400, 3, "bf16"), (1, 64, 128, 4, "f32")])
+@pytest.mark.parametrize("causal", [True, False])
+def test_zigzag_fused_init_finalize_is_bit_identical(heads, d, rows, P, dtype, causal):
+    """ZigzagRing.run with finalize_outs (each piece's init and finalize fused
+    into its first and last product) gives exactly the separate-launch outputs."""
+    wl = synth.Workload(f"zzf_{dtype}_h{heads}_d{d}_c{rows}_p{P}", 250 + rows + d, heads, d, rows,
+                        P, dtype, causal, tuple(range(P)))
+    sub = synth.zigzag_workload(wl)
+    cache = gen_blocks(sub, [(r, b) for b in range(2 * P)
+                             for r in (synth.ROLE_Q, synth.ROLE_K, synth.ROLE_V)])
+    dev = {key: to_device(x, sub) for key, x in cache.items()}
+    for rank in range(P):
+        mine = zigzag_blocks(rank, P)
+        qs = [dev[(synth.ROLE_Q, b)] for b in mine]
+
+        def source(j):
+            a, b = zigzag_blocks(j, P)
+            return (dev[(synth.ROLE_K, a)], dev[(synth.ROLE_K, b)], dev[(synth.ROLE_V, a)],
+                    dev[(synth.ROLE_V, b)])
+
+        ring = ZigzagRing(qs[0].shape, qs[0].dtype)
+        states = [_lib.State(1, heads, sub.rows, d) for _ in range(2)]
+        ring.run(states, qs, source, rank, P, causal, sub.scale)
+        want = [_lib.finalize(st, torch.float32, ring.compute) for st in states]
+        for st in states:
+            for t in (st.m, st.l, st.o):
+                t.fill_(float("nan"))
+        outs = [(torch.empty_like(w[0]), torch.empty_like(w[1])) for w in want]
+        ring.run(states, qs, source, rank, P, causal, sub.scale, finalize_outs=outs)
+        torch.cuda.synchronize()
+        for (o, l), (wo, wlse) in zip(outs, want):
+            assert torch.equal(o, wo) and torch.equal(l, wlse), (rank, causal)
