@@ -128,10 +128,12 @@ def cpu_baseline(wl, rank, blocks, target_s=15.0):
 
 def bench_decode(args, wl):
     """Decode: args.decode_rows query rows (the tokens after the sequence)
-    against the workload's P blocks as key/value shards.  Memory-bound: the
-    figure of merit is the key/value bytes read per second."""
+    against the workload's P blocks as key/value shards, laid out as chunks
+    along the batch axis (ChunkedDecode: one ra_step launch over all shards,
+    log2(P) halving merges, finalize).  Memory-bound: the figure of merit is
+    the key/value bytes read per second."""
     import torch
-    from ring_attention_block_amd.decode import ShardedDecode
+    from ring_attention_block_amd.decode import ChunkedDecode
     from ring_attention_block_amd.hip_events import Event
 
     rq, P, c = args.decode_rows, wl.blocks, wl.rows
@@ -144,19 +146,20 @@ def bench_decode(args, wl):
         return t.reshape(1, *x.shape).to(dev)
 
     q = to_dev(synth.block(wl, synth.ROLE_Q, P, rows=rq))   # the tokens after the cache
-    kv = [(to_dev(blocks[(synth.ROLE_K, j)]), to_dev(blocks[(synth.ROLE_V, j)])) for j in range(P)]
+    k = torch.cat([to_dev(blocks[(synth.ROLE_K, j)]) for j in range(P)], dim=0).contiguous()
+    v = torch.cat([to_dev(blocks[(synth.ROLE_V, j)]) for j in range(P)], dim=0).contiguous()
     compute = torch.cuda.Stream()
-    dec = ShardedDecode(q.shape, P, dev, compute_stream=compute)
+    dec = ChunkedDecode(q.shape, P, dev, compute_stream=compute)
     o = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     for _ in range(args.warmup):
-        dec.run(q, kv, wl.scale, o_out=o, lse_out=lse)
+        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
     torch.cuda.synchronize()
     e0, e1 = Event(timing=True), Event(timing=True)
     t0 = time.perf_counter()
     e0.record(compute)
     for _ in range(args.steps):
-        dec.run(q, kv, wl.scale, o_out=o, lse_out=lse)
+        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
     e1.record(compute)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -172,6 +175,7 @@ def bench_decode(args, wl):
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
         "config": {"workload": wl.name, "mode": "decode", "query_rows": rq, "shards": P,
                    "shard_rows": c, "heads": wl.heads, "head_dim": wl.head_dim,
+                   "layout": "shards as chunks along the batch axis",
                    "kv_bytes": kv_bytes, "flop_per_step": flops,
                    "tflops": round(flops / (ms / 1e3) / 1e12, 2),
                    "pct_of_hbm_peak": round(100 * kv_bytes / (ms / 1e3) / PEAK_HBM_BYTES, 2)},
@@ -312,8 +316,8 @@ def main():
                          "rank i holds pieces i and 2P-1-i")
     ap.add_argument("--decode-rows", type=int, default=None,
                     help="instead of the ring: decode this many query rows against the "
-                         "workload's P blocks as key/value shards (local fold per shard, "
-                         "tree of merges, finalize)")
+                         "workload's P blocks as key/value shards (all shards folded by one "
+                         "launch along the batch axis, halving merges, finalize)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward ring: the rank's backward ring (D, then the "
                          "P gradient steps with dK, dV travelling with the blocks)")

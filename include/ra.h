@@ -22,7 +22,8 @@
  *   - Tensors are dense row-major: q and o are [batch, heads, rows,
  *     head_dim], k and v [batch, heads, kv_rows, head_dim]; m, l and lse are
  *     [batch, heads, rows].  Every non-empty tensor pointer must be 16-byte
- *     aligned.
+ *     aligned, except the state's m and l, which need 4 bytes (so that a
+ *     batch slice of a state is itself a valid state).
  *   - Every call is asynchronous and ordered on `stream` (0 = the null
  *     stream); no call synchronises.  Buffers must stay valid and unmodified
  *     until the stream has passed the call.

@@ -114,6 +114,18 @@ class State:
     def shape(self):
         return (self.c.batch, self.c.heads, self.c.rows, self.c.head_dim)
 
+    def batch_slice(self, start: int, count: int) -> "State":
+        """The state of batch entries [start, start + count), sharing memory."""
+        b, h, r, d = self.shape
+        if start < 0 or count < 0 or start + count > b:
+            raise ValueError(f"batch slice [{start}, {start + count}) outside [0, {b})")
+        view = State.__new__(State)
+        view.m = self.m[start:start + count]
+        view.l = self.l[start:start + count]
+        view.o = self.o[start:start + count]
+        view.c = RaState(count, h, r, d, view.m.data_ptr(), view.l.data_ptr(), view.o.data_ptr())
+        return view
+
 
 def step_case(q_block: int, kv_block: int, num_blocks: int, causal: bool) -> int:
     return _check(lib().ra_step_case(q_block, kv_block, num_blocks, int(causal)))

@@ -29,6 +29,7 @@ ra_status ok() {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
 // Rows of a state (batch * heads * rows) or -1 on a malformed shape.
 // Shape rules shared by every entry point: rows >= 0, head_dim 64 or 128, and
@@ -59,8 +60,8 @@ ra_status check_state(const ra_state *st, const char *name, int64_t *n_rows) {
   if (n > 0) {
     if (!st->m || !st->l || !st->o)
       return fail(RA_ERR_INVALID_ARG, "%s: NULL m, l or o with %lld rows", name, (long long)n);
-    if (!aligned16(st->m) || !aligned16(st->l) || !aligned16(st->o))
-      return fail(RA_ERR_INVALID_ARG, "%s: m, l and o must be 16-byte aligned", name);
+    if (!aligned4(st->m) || !aligned4(st->l) || !aligned16(st->o))
+      return fail(RA_ERR_INVALID_ARG, "%s: o must be 16-byte aligned, m and l 4-byte aligned", name);
   }
   *n_rows = n;
   return RA_OK;

@@ -241,8 +241,9 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], RowState &rs, bf1
 }
 
 // kMask: some tile may need the element mask (diagonal block, or a block
-// length that is not a multiple of 64).
-template <int D, bool kDiag, int kW, bool kMask>
+// length that is not a multiple of 64).  kIdle: the query rows are not a
+// multiple of the workgroup's, so some wavefronts may have no rows.
+template <int D, bool kDiag, int kW, bool kMask, bool kIdle>
 __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D>;
@@ -417,8 +418,13 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
         oacc[b][4 * g + 3] = x.w;
       }
   }
+  // kIdle: some wavefront's rows may all lie past the block end (a short
+  // query block, as in decoding); such a wavefront only issues its share of
+  // the copies and takes the barriers.  Without kIdle the test compiles away
+  // (the kernel without it is scheduled better).
+  const bool wave_active = !kIdle || q0w < rows;
   f32x16 s_cur[2];
-  {
+  if (wave_active) {
     scores(s_cur, lds_k0);   // tile 0 is never skipped
     if (kMask && mask_needed(0)) mask_tile(s_cur, h * 8, lim);
     bool rescale;
@@ -443,53 +449,55 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     if (t + 1 < n_tiles) issue_copy<D, kW>(v_dst, rv, so.v, (t + 1) * kBN, wave);
     const bool has_next = t + 1 < n_tiles;
 
-    f32x16 s_nxt[2];
-    bf16x8 pb[4];
-    bool rescale = false;
-    float alpha = 1.f;
-    if constexpr (kFast) {
-      // The scores of the tile after the last one read a stale K buffer;
-      // has_next = false keeps them out of the state.
-      scores(s_nxt, k_src);
-      tile_exp(s_cur, rs, pb, sl2);
-      accumulate(pb, v_src);
-      alpha = tile_max_update(s_nxt, rs, sl2, has_next, rescale);
-      // Interleave: per score MFMA one LDS read and four vector instructions
-      // (exponentials of tile t), then per P V MFMA two LDS reads and up to
-      // four vector instructions (the rest of the exponentials, then the row
-      // maximum of tile t+1).  The slots cover every vector instruction of
-      // the block, so none is left for a serial tail after the last MFMA.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * kQK; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4 * kDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
-      }
-    } else {
-      const bool run_next = has_next && !skip_tile(t + 1);
-      if (run_next) scores(s_nxt, k_src);
-      if (!skip_tile(t)) {
+    if (wave_active) {
+      f32x16 s_nxt[2];
+      bf16x8 pb[4];
+      bool rescale = false;
+      float alpha = 1.f;
+      if constexpr (kFast) {
+        // The scores of the tile after the last one read a stale K buffer;
+        // has_next = false keeps them out of the state.
+        scores(s_nxt, k_src);
         tile_exp(s_cur, rs, pb, sl2);
         accumulate(pb, v_src);
-      }
-      if (run_next) {
-        if (mask_needed(t + 1)) mask_tile(s_nxt, (t + 1) * kBN + h * 8, lim);
-        alpha = tile_max_update(s_nxt, rs, sl2, true, rescale);
-      }
-    }
-    if (rescale) {
+        alpha = tile_max_update(s_nxt, rs, sl2, has_next, rescale);
+        // Interleave: per score MFMA one LDS read and four vector instructions
+        // (exponentials of tile t), then per P V MFMA two LDS reads and up to
+        // four vector instructions (the rest of the exponentials, then the row
+        // maximum of tile t+1).  The slots cover every vector instruction of
+        // the block, so none is left for a serial tail after the last MFMA.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
-    }
+        for (int i = 0; i < 2 * kQK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+        }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) s_cur[sb] = s_nxt[sb];
+        for (int i = 0; i < 4 * kDB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 4, 0);
+        }
+      } else {
+        const bool run_next = has_next && !skip_tile(t + 1);
+        if (run_next) scores(s_nxt, k_src);
+        if (!skip_tile(t)) {
+          tile_exp(s_cur, rs, pb, sl2);
+          accumulate(pb, v_src);
+        }
+        if (run_next) {
+          if (mask_needed(t + 1)) mask_tile(s_nxt, (t + 1) * kBN + h * 8, lim);
+          alpha = tile_max_update(s_nxt, rs, sl2, true, rescale);
+        }
+      }
+      if (rescale) {
+#pragma unroll
+        for (int b = 0; b < kDB; ++b) oacc[b] *= alpha;
+      }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) s_cur[sb] = s_nxt[sb];
+    }
     __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of K(t+2), V(t+1) landed
     __syncthreads();
   };
@@ -594,10 +602,16 @@ hipError_t launch(const StepArgs &a, hipStream_t s) {
   const int n_qt = (a.rows + kBM - 1) / kBM;
   const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(64 * kW);
   if constexpr (kDiag) {
-    step_bf16_kernel<D, true, kW, true><<<grid, block, 0, s>>>(a);
+    step_bf16_kernel<D, true, kW, true, false><<<grid, block, 0, s>>>(a);
   } else {
-    if (a.kv_rows % kBN != 0) step_bf16_kernel<D, false, kW, true><<<grid, block, 0, s>>>(a);
-    else step_bf16_kernel<D, false, kW, false><<<grid, block, 0, s>>>(a);
+    const bool mask = a.kv_rows % kBN != 0, idle = a.rows % kBM != 0;
+    if (mask) {
+      if (idle) step_bf16_kernel<D, false, kW, true, true><<<grid, block, 0, s>>>(a);
+      else step_bf16_kernel<D, false, kW, true, false><<<grid, block, 0, s>>>(a);
+    } else {
+      if (idle) step_bf16_kernel<D, false, kW, false, true><<<grid, block, 0, s>>>(a);
+      else step_bf16_kernel<D, false, kW, false, false><<<grid, block, 0, s>>>(a);
+    }
   }
   return hipGetLastError();
 }

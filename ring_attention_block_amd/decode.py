@@ -73,3 +73,51 @@ class ShardedDecode:
                 _lib.lse_merge(self.states[dst], self.states[src], self.compute)
         return _lib.finalize(self.states[0], out_dtype, self.compute, o_out=o_out,
                              lse_out=lse_out)
+
+
+class ChunkedDecode:
+    """Decode with the key/value cache laid out as chunks along the batch axis.
+
+    The cache (all shards) is held as K, V of shape [chunks, heads, chunk_rows,
+    head_dim]: chunk c is a contiguous [heads, chunk_rows, head_dim] slab.  The
+    query block [1, heads, rows, head_dim] is broadcast to every chunk and one
+    ra_step launch folds all chunks at once (batch = chunks, so every chunk and
+    head has its own workgroups); the chunks' partial states are then reduced
+    by log2(chunks) ra_lse_merge launches, each merging the second half of the
+    remaining batch into the first (the merge is associative and commutative
+    up to rounding), and chunk 0 is finalized.  All on one stream, with no
+    cross-stream synchronisation.  chunks must be a power of two.
+    """
+
+    def __init__(self, q_shape, chunks: int, device="cuda", compute_stream=None):
+        b, h, rows, d = q_shape
+        if b != 1:
+            raise ValueError("the query block must have batch 1")
+        if chunks < 1 or chunks & (chunks - 1):
+            raise ValueError(f"chunks={chunks} must be a power of two")
+        self.chunks = chunks
+        self.q_shape = tuple(q_shape)
+        self.state = _lib.State(chunks, h, rows, d, device=device)
+        self.qb = torch.empty((chunks, h, rows, d), dtype=torch.bfloat16, device=device)
+        self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
+            out_dtype=torch.float32, o_out=None, lse_out=None):
+        """k, v: [chunks, heads, chunk_rows, head_dim].  Returns the finalized
+        (O, LSE) of q against all chunks."""
+        n = self.chunks
+        if tuple(k.shape[:2]) != (n, self.q_shape[1]) or k.shape != v.shape:
+            raise ValueError(f"k, v must be [{n}, {self.q_shape[1]}, chunk_rows, d]")
+        if self.qb.dtype != q.dtype:
+            self.qb = torch.empty(self.qb.shape, dtype=q.dtype, device=self.qb.device)
+        with torch.cuda.stream(self.compute):
+            self.qb.copy_(q.expand(n, -1, -1, -1))
+        _lib.step(self.state, self.qb, k, v, 0, 0, 1, False, scale, self.compute,
+                  flags=_lib.RA_STEP_FRESH)
+        width = n
+        while width > 1:
+            width //= 2
+            _lib.lse_merge(self.state.batch_slice(0, width), self.state.batch_slice(width, width),
+                           self.compute)
+        return _lib.finalize(self.state.batch_slice(0, 1), out_dtype, self.compute, o_out=o_out,
+                             lse_out=lse_out)

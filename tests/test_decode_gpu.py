@@ -98,3 +98,46 @@ def test_unequal_block_step_matches_merge_of_halves():
     # oracle tolerance each of them meets.
     assert_close(o1.cpu().numpy(), o2.cpu().numpy(), 2e-3, "O whole vs merged halves")
     assert_close(lse1.cpu().numpy(), lse2.cpu().numpy(), 2e-3, "LSE whole vs merged halves")
+
+
+CHUNKED = [
+    # (heads, head_dim, query rows, chunk rows, chunks, dtype)
+    (2, 128, 1, 512, 8, "bf16"),
+    (4, 128, 16, 1000, 4, "bf16"),
+    (3, 64, 64, 200, 2, "bf16"),
+    (2, 64, 5, 129, 4, "f32"),
+    (1, 128, 300, 64, 1, "f32"),
+    (2, 128, 7, 333, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("heads,d,rq,c,n,dtype", CHUNKED)
+def test_chunked_decode(heads, d, rq, c, n, dtype):
+    """ChunkedDecode (the cache as n chunks along the batch axis, one ra_step
+    launch over all chunks, halving merges, finalize) against the oracle over
+    the whole cache."""
+    from ring_attention_block_amd.decode import ChunkedDecode
+    wl = synth.Workload(f"cdec_{dtype}_h{heads}_d{d}_q{rq}_c{c}_n{n}", 600 + rq + c, heads, d, c,
+                        n + 1, dtype, False, (n,))
+    _say(wl.name)
+    qh = synth.block(wl, synth.ROLE_Q, n, rows=rq)
+    kh = [synth.block(wl, synth.ROLE_K, j) for j in range(n)]
+    vh = [synth.block(wl, synth.ROLE_V, j) for j in range(n)]
+    q = to_device(qh, wl)
+    k = torch.cat([to_device(x, wl) for x in kh], dim=0).contiguous()
+    v = torch.cat([to_device(x, wl) for x in vh], dim=0).contiguous()
+    dec = ChunkedDecode(q.shape, n)
+    for _ in range(2):   # the second call reuses the states of the first
+        o, lse = dec.run(q, k, v, wl.scale)
+    torch.cuda.synchronize()
+    to, tl = tol_for(wl)
+    kp, qp = np.arange(n * c), np.full(rq, n * c)
+    for hh in range(heads):
+        want_o, want_lse = dense.attention(
+            oracle_values(qh[hh:hh + 1], wl),
+            np.concatenate([oracle_values(x[hh:hh + 1], wl) for x in kh], axis=1),
+            np.concatenate([oracle_values(x[hh:hh + 1], wl) for x in vh], axis=1),
+            qp, kp, False, wl.scale)
+        eo = assert_close(o[0, hh].cpu().numpy(), want_o[0], to, f"head {hh} O")
+        el = assert_close(lse[0, hh].cpu().numpy(), want_lse[0], tl, f"head {hh} LSE")
+    _say(f"  max|dO|={eo:.2e} max|dLSE|={el:.2e} (last head)")
