@@ -449,7 +449,8 @@ def main():
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
 
     line = {
-        "metric": "causal bf16 ring-step attention TFLOP/s + % of MFMA peak (c=4096, d=128)",
+        "metric": (f"{'causal' if wl.causal else 'non-causal'} {wl.dtype} ring-step attention "
+                   f"TFLOP/s + % of MFMA peak (c={wl.rows}, d={wl.head_dim})"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
