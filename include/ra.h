@@ -158,6 +158,27 @@ ra_status ra_step_ex(ra_state *st, const void *q, const void *k, const void *v, 
                      float *lse_out, hipStream_t stream);
 
 /*
+ * ra_step_ex for a caller that times every step while the ring runs (the
+ * per-kernel durations of a profiler's kernel trace, taken live).  Arguments
+ * as in ra_step_ex, plus two HIP events, created by the caller with timing
+ * enabled on the device of `stream` (either may be NULL; the caller keeps
+ * ownership and may reuse them once the stream has passed this call):
+ *   start, stop   when the call folds a block, they take the begin and end
+ *                 timestamps of the step kernel's own dispatch packet
+ *                 (hipExtLaunchKernel), so timing adds no marker between two
+ *                 steps on the stream; when it folds nothing (a skipped
+ *                 block, kv_rows == 0, an empty state), start is recorded on
+ *                 the stream before whatever the flags enqueue and stop after.
+ * Results are those of ra_step_ex.  On an error return nothing is enqueued
+ * and neither event is recorded.
+ */
+ra_status ra_step_timed(ra_state *st, const void *q, const void *k, const void *v,
+                        ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
+                        int32_t num_blocks, int32_t causal, float scale, uint32_t flags,
+                        void *o_out, ra_dtype out_dtype, float *lse_out, hipEvent_t start,
+                        hipEvent_t stop, hipStream_t stream);
+
+/*
  * dst <- dst (+) src: merge two partial states over disjoint key sets
  * (aicassindra architecture article, section "The architecture: every piece
  * explained": take the larger maximum, rescale each side by exp(its max - new
@@ -240,6 +261,19 @@ ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_d
                       const void *v, ra_dtype in_dtype, float *dq, float *dk, float *dv,
                       int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
                       float scale, hipStream_t stream);
+
+/*
+ * ra_bwd_step with timing events as in ra_step_timed: start takes the begin
+ * of the step's first kernel, stop the end of its last (bf16: the dq kernel,
+ * then the dk/dv kernel; fp32: one kernel); a skipped block records both on
+ * the stream back to back.  Results are those of ra_bwd_step.
+ */
+ra_status ra_bwd_step_timed(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
+                            const void *q, const void *dout, const float *lse, const float *delta,
+                            const void *k, const void *v, ra_dtype in_dtype, float *dq, float *dk,
+                            float *dv, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                            int32_t causal, float scale, hipEvent_t start, hipEvent_t stop,
+                            hipStream_t stream);
 
 /* Static string naming a status code. */
 const char *ra_status_string(ra_status s);

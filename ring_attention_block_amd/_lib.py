@@ -19,8 +19,9 @@ RA_F32, RA_BF16 = 0, 1
 RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
 
 # Every symbol include/ra.h declares.
-EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_lse_merge", "ra_finalize",
-           "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_status_string", "ra_last_error")
+EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_step_timed", "ra_lse_merge",
+           "ra_finalize", "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_bwd_step_timed",
+           "ra_status_string", "ra_last_error")
 
 
 class RaState(ctypes.Structure):
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
             "ra_step": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32, vp]),
             "ra_step_ex": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, f32,
                                           ctypes.c_uint32, vp, ctypes.c_int, vp, vp]),
+            "ra_step_timed": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32,
+                                             f32, ctypes.c_uint32, vp, ctypes.c_int, vp, vp, vp, vp]),
             "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
             "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
@@ -60,6 +63,9 @@ def lib() -> ctypes.CDLL:
                                               vp, vp]),
             "ra_bwd_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                            vp, vp, vp, i32, i32, i32, i32, f32, vp]),
+            "ra_bwd_step_timed": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                                 ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, f32,
+                                                 vp, vp, vp]),
             "ra_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "ra_last_error": (ctypes.c_char_p, []),
         }
@@ -95,6 +101,13 @@ def _stream(stream) -> int | None:
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def _event(ev) -> int | None:
+    """A hipEvent_t from an event object with a .handle, a raw handle, or None."""
+    if ev is None:
+        return None
+    return ev.handle if hasattr(ev, "handle") else ev
 
 
 class State:
@@ -147,12 +160,15 @@ RA_STEP_FRESH, RA_STEP_FINALIZE = 1, 2
 
 
 def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
-         scale: float, stream=None, flags: int = 0, o_out=None, lse_out=None) -> int:
+         scale: float, stream=None, flags: int = 0, o_out=None, lse_out=None, start=None,
+         stop=None) -> int:
     """Fold block kv_block into st; returns the causal case (0 skip, 1 diag, 2 full).
 
     flags (ra_step_ex): RA_STEP_FRESH starts from the empty state without
     reading st; RA_STEP_FINALIZE writes o_out (fp32 or bf16) and lse_out
-    instead of st, as finalize would.
+    instead of st, as finalize would.  start, stop (ra_step_timed): timing
+    events (objects with a .handle, or raw hipEvent_t values) that take the
+    begin and end of the step kernel's dispatch.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_contiguous():
@@ -164,7 +180,7 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
         raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if tuple(q.shape) != st.shape:
         raise ValueError(f"q shape {tuple(q.shape)} does not match the state {st.shape}")
-    if flags == 0:
+    if flags == 0 and start is None and stop is None:
         _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
                              k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
                              _stream(stream)))
@@ -177,9 +193,13 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
                                     or lse_out.dtype != torch.float32):
             raise ValueError("lse_out must be a contiguous fp32 [B,H,rows] tensor")
         out_code = RA_BF16 if o_out is not None and o_out.dtype == torch.bfloat16 else RA_F32
-        _check(lib().ra_step_ex(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
-                                k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
-                                int(flags), _ptr(o_out), out_code, _ptr(lse_out), _stream(stream)))
+        args = (ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), k.shape[2], q_block,
+                kv_block, num_blocks, int(causal), float(scale), int(flags), _ptr(o_out), out_code,
+                _ptr(lse_out))
+        if start is None and stop is None:
+            _check(lib().ra_step_ex(*args, _stream(stream)))
+        else:
+            _check(lib().ra_step_timed(*args, _event(start), _event(stop), _stream(stream)))
     return step_case(q_block, kv_block, num_blocks, causal)
 
 
@@ -224,9 +244,11 @@ def bwd_prepare(o, dout, delta=None, stream=None):
 
 
 def bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_block: int, kv_block: int,
-             num_blocks: int, causal: bool, scale: float, stream=None) -> int:
+             num_blocks: int, causal: bool, scale: float, stream=None, start=None,
+             stop=None) -> int:
     """Add block kv_block's backward contribution: dq += ..., dk += ..., dv += ...
-    Returns the causal case."""
+    start, stop (ra_bwd_step_timed): timing events bound to the step's first
+    and last kernel dispatch.  Returns the causal case."""
     tensors = (("q", q), ("dout", dout), ("k", k), ("v", v), ("dq", dq), ("dk", dk), ("dv", dv))
     for name, t in tensors:
         if not t.is_contiguous() or tuple(t.shape) != tuple(q.shape):
@@ -239,7 +261,11 @@ def bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_block: int, kv_block: int,
     for name, t in (("lse", lse), ("delta", delta)):
         if t.dtype != torch.float32 or tuple(t.shape) != (b, h, r) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float32 [B,H,rows] tensor")
-    _check(lib().ra_bwd_step(b, h, r, d, _ptr(q), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(k),
-                             _ptr(v), _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), q_block,
-                             kv_block, num_blocks, int(causal), float(scale), _stream(stream)))
+    args = (b, h, r, d, _ptr(q), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(k), _ptr(v),
+            _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), q_block, kv_block, num_blocks,
+            int(causal), float(scale))
+    if start is None and stop is None:
+        _check(lib().ra_bwd_step(*args, _stream(stream)))
+    else:
+        _check(lib().ra_bwd_step_timed(*args, _event(start), _event(stop), _stream(stream)))
     return step_case(q_block, kv_block, num_blocks, causal)

@@ -155,12 +155,11 @@ __global__ void __launch_bounds__(kThreads) bwd_step_simple_kernel(BwdArgs a) {
 }
 
 template <int D, typename T>
-hipError_t launch_simple_d(const BwdArgs &a, bool diag, hipStream_t s) {
+hipError_t launch_simple_d(const BwdArgs &a, bool diag, hipStream_t s, const LaunchTiming &t) {
   const int n_qt = (a.rows + kRows - 1) / kRows;
   const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(kThreads);
-  if (diag) bwd_step_simple_kernel<D, true, T><<<grid, block, 0, s>>>(a);
-  else bwd_step_simple_kernel<D, false, T><<<grid, block, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_one(diag ? bwd_step_simple_kernel<D, true, T> : bwd_step_simple_kernel<D, false, T>,
+                    grid, block, s, t.start, t.stop, a);
 }
 
 template <int D>
@@ -186,11 +185,13 @@ hipError_t launch_bwd_prepare(const void *o, bool o_bf16, const void *dout, bool
   return launch_prepare_d<64>(o, o_bf16, dout, do_bf16, delta, n_rows, s);
 }
 
-hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s) {
+hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s,
+                                  const LaunchTiming &t) {
   const bool diag = c == StepCase::Diag;
   if (d == 128)
-    return bf16 ? launch_simple_d<128, uint16_t>(a, diag, s) : launch_simple_d<128, float>(a, diag, s);
-  return bf16 ? launch_simple_d<64, uint16_t>(a, diag, s) : launch_simple_d<64, float>(a, diag, s);
+    return bf16 ? launch_simple_d<128, uint16_t>(a, diag, s, t)
+                : launch_simple_d<128, float>(a, diag, s, t);
+  return bf16 ? launch_simple_d<64, uint16_t>(a, diag, s, t) : launch_simple_d<64, float>(a, diag, s, t);
 }
 
 }  // namespace ra

@@ -633,24 +633,24 @@ __global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_k
 }
 
 template <int D, bool kDiag>
-hipError_t launch_d(const BwdArgs &a, hipStream_t s) {
+hipError_t launch_d(const BwdArgs &a, hipStream_t s, const LaunchTiming &t) {
   constexpr int kB = 32 * kWaves;
   const int n_t = (a.rows + kB - 1) / kB;
   const dim3 grid((unsigned)((int64_t)a.bh * n_t)), block(64 * kWaves);
-  if (kDiag || a.rows % kBT != 0) bwd_dq_bf16_kernel<D, kDiag, true><<<grid, block, 0, s>>>(a);
-  else bwd_dq_bf16_kernel<D, kDiag, false><<<grid, block, 0, s>>>(a);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_one((kDiag || a.rows % kBT != 0) ? bwd_dq_bf16_kernel<D, kDiag, true>
+                                                               : bwd_dq_bf16_kernel<D, kDiag, false>,
+                                  grid, block, s, t.start, nullptr, a);
   if (e != hipSuccess) return e;
-  bwd_dkdv_bf16_kernel<D, kDiag><<<grid, block, 0, s>>>(a);
-  return hipGetLastError();
+  return launch_one(bwd_dkdv_bf16_kernel<D, kDiag>, grid, block, s, nullptr, t.stop, a);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_step_bf16(const BwdArgs &a, int d, StepCase c, hipStream_t s) {
+hipError_t launch_bwd_step_bf16(const BwdArgs &a, int d, StepCase c, hipStream_t s,
+                                const LaunchTiming &t) {
   const bool diag = c == StepCase::Diag;
-  if (d == 128) return diag ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
-  if (d == 64) return diag ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+  if (d == 128) return diag ? launch_d<128, true>(a, s, t) : launch_d<128, false>(a, s, t);
+  if (d == 64) return diag ? launch_d<64, true>(a, s, t) : launch_d<64, false>(a, s, t);
   return hipErrorInvalidValue;
 }
 

@@ -124,7 +124,8 @@ namespace {
 ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k, const void *v,
                     ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
                     int32_t num_blocks, int32_t causal, float scale, uint32_t flags, void *o_out,
-                    ra_dtype out_dtype, float *lse_out, hipStream_t stream) {
+                    ra_dtype out_dtype, float *lse_out, hipEvent_t start, hipEvent_t stop,
+                    hipStream_t stream) {
   int64_t n = 0;
   ra_status s = check_state(st, name, &n);
   if (s != RA_OK) return s;
@@ -160,14 +161,27 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
         return fail(RA_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", name);
     }
   }
-  if (n == 0) return ok();
-  if (c == RA_CASE_SKIP || kv_rows == 0) {
-    // Nothing to fold: the flags still take effect through the state kernels.
-    if (flags & RA_STEP_FRESH) {
+  if (n == 0 || c == RA_CASE_SKIP || kv_rows == 0) {
+    // Nothing to fold: the flags still take effect through the state kernels,
+    // and the timing events bracket whatever they enqueue.
+    if (start) {
+      (void)hipGetLastError();
+      const hipError_t e = hipEventRecord(start, stream);
+      if (e != hipSuccess) return hip_status(e, name);
+    }
+    if (n > 0 && (flags & RA_STEP_FRESH)) {
       s = ra_state_init(st, stream);
       if (s != RA_OK) return s;
     }
-    if (flags & RA_STEP_FINALIZE) return ra_finalize(st, o_out, out_dtype, lse_out, stream);
+    if (n > 0 && (flags & RA_STEP_FINALIZE)) {
+      s = ra_finalize(st, o_out, out_dtype, lse_out, stream);
+      if (s != RA_OK) return s;
+    }
+    if (stop) {
+      (void)hipGetLastError();
+      const hipError_t e = hipEventRecord(stop, stream);
+      if (e != hipSuccess) return hip_status(e, name);
+    }
     return ok();
   }
 
@@ -188,8 +202,9 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   a.out_bf16 = out_dtype == RA_BF16;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
   (void)hipGetLastError();
-  const hipError_t e = in_dtype == RA_BF16 ? ra::launch_step_bf16(a, st->head_dim, sc, stream)
-                                           : ra::launch_step_f32(a, st->head_dim, sc, stream);
+  const ra::LaunchTiming t{start, stop};
+  const hipError_t e = in_dtype == RA_BF16 ? ra::launch_step_bf16(a, st->head_dim, sc, stream, t)
+                                           : ra::launch_step_f32(a, st->head_dim, sc, stream, t);
   return hip_status(e, name);
 }
 
@@ -199,7 +214,7 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
                   int32_t kv_rows, int32_t q_block, int32_t kv_block, int32_t num_blocks,
                   int32_t causal, float scale, hipStream_t stream) {
   return step_impl("ra_step", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks, causal,
-                   scale, 0u, nullptr, RA_F32, nullptr, stream);
+                   scale, 0u, nullptr, RA_F32, nullptr, nullptr, nullptr, stream);
 }
 
 ra_status ra_step_ex(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,
@@ -207,7 +222,16 @@ ra_status ra_step_ex(ra_state *st, const void *q, const void *k, const void *v, 
                      int32_t causal, float scale, uint32_t flags, void *o_out, ra_dtype out_dtype,
                      float *lse_out, hipStream_t stream) {
   return step_impl("ra_step_ex", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks,
-                   causal, scale, flags, o_out, out_dtype, lse_out, stream);
+                   causal, scale, flags, o_out, out_dtype, lse_out, nullptr, nullptr, stream);
+}
+
+ra_status ra_step_timed(ra_state *st, const void *q, const void *k, const void *v,
+                        ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
+                        int32_t num_blocks, int32_t causal, float scale, uint32_t flags,
+                        void *o_out, ra_dtype out_dtype, float *lse_out, hipEvent_t start,
+                        hipEvent_t stop, hipStream_t stream) {
+  return step_impl("ra_step_timed", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks,
+                   causal, scale, flags, o_out, out_dtype, lse_out, start, stop, stream);
 }
 
 ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream) {
@@ -263,30 +287,40 @@ ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t hea
                     "ra_bwd_prepare launch");
 }
 
-ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim, const void *q,
-                      const void *dout, const float *lse, const float *delta, const void *k,
-                      const void *v, ra_dtype in_dtype, float *dq, float *dk, float *dv,
-                      int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
-                      float scale, hipStream_t stream) {
+static ra_status bwd_impl(const char *name, int32_t batch, int32_t heads, int32_t rows,
+                          int32_t head_dim, const void *q, const void *dout, const float *lse,
+                          const float *delta, const void *k, const void *v, ra_dtype in_dtype,
+                          float *dq, float *dk, float *dv, int32_t q_block, int32_t kv_block,
+                          int32_t num_blocks, int32_t causal, float scale, hipEvent_t start,
+                          hipEvent_t stop, hipStream_t stream) {
   int64_t n = 0;
-  ra_status s = check_shape(batch, heads, rows, head_dim, "ra_bwd_step", &n);
+  ra_status s = check_shape(batch, heads, rows, head_dim, name, &n);
   if (s != RA_OK) return s;
   const int32_t c = ra_step_case(q_block, kv_block, num_blocks, causal);
   if (c < 0) return (ra_status)c;
   if (in_dtype != RA_F32 && in_dtype != RA_BF16)
-    return fail(RA_ERR_INVALID_ARG, "ra_bwd_step: in_dtype=%d is not RA_F32 or RA_BF16", (int)in_dtype);
+    return fail(RA_ERR_INVALID_ARG, "%s: in_dtype=%d is not RA_F32 or RA_BF16", name, (int)in_dtype);
   if (in_dtype == RA_BF16 && bf16_block_too_long(rows, head_dim))
-    return fail(RA_ERR_UNSUPPORTED, "ra_bwd_step: bf16 blocks are limited to 2^31 bytes per (batch, head)");
+    return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks are limited to 2^31 bytes per (batch, head)", name);
   if (!(scale > 0.f) || !isfinite(scale))
-    return fail(RA_ERR_INVALID_ARG, "ra_bwd_step: scale=%g must be finite and > 0", (double)scale);
+    return fail(RA_ERR_INVALID_ARG, "%s: scale=%g must be finite and > 0", name, (double)scale);
   if (n > 0) {
     const void *ptrs[] = {q, dout, lse, delta, k, v, dq, dk, dv};
     for (const void *p : ptrs)
       if (!p || !aligned16(p))
         return fail(RA_ERR_INVALID_ARG,
-                    "ra_bwd_step: q, dout, lse, delta, k, v, dq, dk, dv must be non-NULL and 16-byte aligned");
+                    "%s: q, dout, lse, delta, k, v, dq, dk, dv must be non-NULL and 16-byte aligned", name);
   }
-  if (c == RA_CASE_SKIP || n == 0) return ok();
+  if (c == RA_CASE_SKIP || n == 0) {
+    // Nothing to add: the timing events are recorded back to back.
+    for (hipEvent_t ev : {start, stop}) {
+      if (!ev) continue;
+      (void)hipGetLastError();
+      const hipError_t e = hipEventRecord(ev, stream);
+      if (e != hipSuccess) return hip_status(e, name);
+    }
+    return ok();
+  }
   ra::BwdArgs a;
   a.q = q;
   a.dout = dout;
@@ -303,11 +337,34 @@ ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_d
   a.scale_log2 = scale * 1.442695040888963407f;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
   (void)hipGetLastError();
+  const ra::LaunchTiming t{start, stop};
   const hipError_t e = in_dtype == RA_BF16
-                          ? ra::launch_bwd_step_bf16(a, head_dim, sc, stream)
-                          : ra::launch_bwd_step_simple(a, head_dim, in_dtype == RA_BF16, sc, stream);
-  return hip_status(e, "ra_bwd_step launch");
+                          ? ra::launch_bwd_step_bf16(a, head_dim, sc, stream, t)
+                          : ra::launch_bwd_step_simple(a, head_dim, false, sc, stream, t);
+  return hip_status(e, name);
 }
+
+ra_status ra_bwd_step(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim, const void *q,
+                      const void *dout, const float *lse, const float *delta, const void *k,
+                      const void *v, ra_dtype in_dtype, float *dq, float *dk, float *dv,
+                      int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
+                      float scale, hipStream_t stream) {
+  return bwd_impl("ra_bwd_step", batch, heads, rows, head_dim, q, dout, lse, delta, k, v, in_dtype,
+                  dq, dk, dv, q_block, kv_block, num_blocks, causal, scale, nullptr, nullptr, stream);
+}
+
+ra_status ra_bwd_step_timed(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
+                            const void *q, const void *dout, const float *lse, const float *delta,
+                            const void *k, const void *v, ra_dtype in_dtype, float *dq, float *dk,
+                            float *dv, int32_t q_block, int32_t kv_block, int32_t num_blocks,
+                            int32_t causal, float scale, hipEvent_t start, hipEvent_t stop,
+                            hipStream_t stream) {
+  return bwd_impl("ra_bwd_step_timed", batch, heads, rows, head_dim, q, dout, lse, delta, k, v,
+                  in_dtype, dq, dk, dv, q_block, kv_block, num_blocks, causal, scale, start, stop,
+                  stream);
+}
+
+
 
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return ok();

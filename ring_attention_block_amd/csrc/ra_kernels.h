@@ -3,6 +3,7 @@
 // enqueue and return the hipError_t of the launch.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,20 +46,42 @@ struct BwdArgs {
   float scale_log2;              // scale * log2(e)
 };
 
+// Timestamps of a launch for a caller that times it: the events (either may
+// be null) take the begin and the end of the kernel's own dispatch packet, so
+// timing adds no marker to the stream.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+// kernel(arg) on s, with start and stop (may be null) bound to the dispatch.
+template <typename Arg>
+hipError_t launch_one(void (*kernel)(Arg), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start,
+                      hipEvent_t stop, Arg arg) {
+  void *args[] = {&arg};
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, s, start,
+                            stop, 0);
+}
+
 hipError_t launch_state_init(float *m, float *l, float *o, int64_t n_rows, int d,
                              hipStream_t s);
 hipError_t launch_state_merge(float *dm, float *dl, float *dO, const float *sm, const float *sl,
                               const float *sO, int64_t n_rows, int d, hipStream_t s);
 hipError_t launch_finalize(const float *m, const float *l, const float *o, void *o_out,
                            bool out_bf16, float *lse, int64_t n_rows, int d, hipStream_t s);
-hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s);
-hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s);
+hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s,
+                            const LaunchTiming &t = {});
+hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s,
+                           const LaunchTiming &t = {});
 // bytes a multiple of 16, both pointers 16-byte aligned, no overlap.
 hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
 hipError_t launch_bwd_prepare(const void *o, bool o_bf16, const void *dout, bool do_bf16,
                               float *delta, int64_t n_rows, int d, hipStream_t s);
-hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s);
-// Matrix-core backward step (bf16, head_dim 64 or 128).
-hipError_t launch_bwd_step_bf16(const BwdArgs &a, int d, StepCase c, hipStream_t s);
+hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s,
+                                  const LaunchTiming &t = {});
+// Matrix-core backward step (bf16, head_dim 64 or 128): two kernels; t.start
+// is bound to the first, t.stop to the second.
+hipError_t launch_bwd_step_bf16(const BwdArgs &a, int d, StepCase c, hipStream_t s,
+                                const LaunchTiming &t = {});
 
 }  // namespace ra

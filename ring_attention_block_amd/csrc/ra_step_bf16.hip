@@ -597,23 +597,21 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
 }
 
 template <int D, bool kDiag, int kW>
-hipError_t launch(const StepArgs &a, hipStream_t s) {
+hipError_t launch(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
   constexpr int kBM = 32 * kW;
   const int n_qt = (a.rows + kBM - 1) / kBM;
   const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(64 * kW);
-  if constexpr (kDiag) {
-    step_bf16_kernel<D, true, kW, true, false><<<grid, block, 0, s>>>(a);
-  } else {
-    const bool mask = a.kv_rows % kBN != 0, idle = a.rows % kBM != 0;
-    if (mask) {
-      if (idle) step_bf16_kernel<D, false, kW, true, true><<<grid, block, 0, s>>>(a);
-      else step_bf16_kernel<D, false, kW, true, false><<<grid, block, 0, s>>>(a);
-    } else {
-      if (idle) step_bf16_kernel<D, false, kW, false, true><<<grid, block, 0, s>>>(a);
-      else step_bf16_kernel<D, false, kW, false, false><<<grid, block, 0, s>>>(a);
-    }
+  auto go = [&](void (*kernel)(StepArgs)) {
+    return launch_one(kernel, grid, block, s, t.start, t.stop, a);
+  };
+  if constexpr (kDiag) return go(step_bf16_kernel<D, true, kW, true, false>);
+  const bool mask = a.kv_rows % kBN != 0, idle = a.rows % kBM != 0;
+  if (mask) {
+    return idle ? go(step_bf16_kernel<D, false, kW, true, true>)
+                : go(step_bf16_kernel<D, false, kW, true, false>);
   }
-  return hipGetLastError();
+  return idle ? go(step_bf16_kernel<D, false, kW, false, true>)
+              : go(step_bf16_kernel<D, false, kW, false, false>);
 }
 
 // Full blocks: 8-wavefront workgroups (256 query rows share each key/value
@@ -626,21 +624,22 @@ hipError_t launch(const StepArgs &a, hipStream_t s) {
 constexpr int64_t kComputeUnits = 256;
 
 template <int D, bool kDiag>
-hipError_t launch_d(const StepArgs &a, hipStream_t s) {
+hipError_t launch_d(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
   if constexpr (kDiag) {
-    return launch<D, kDiag, 4>(a, s);
+    return launch<D, kDiag, 4>(a, s, t);
   } else {
-    if ((int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s);
-    return launch<D, kDiag, 8>(a, s);
+    if ((int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s, t);
+    return launch<D, kDiag, 8>(a, s, t);
   }
 }
 
 }  // namespace
 
-hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s) {
+hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s,
+                            const LaunchTiming &t) {
   const bool diag = c == StepCase::Diag;
-  if (d == 128) return diag ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
-  return diag ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
+  if (d == 128) return diag ? launch_d<128, true>(a, s, t) : launch_d<128, false>(a, s, t);
+  return diag ? launch_d<64, true>(a, s, t) : launch_d<64, false>(a, s, t);
 }
 
 }  // namespace ra

@@ -128,18 +128,14 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
 
 }  // namespace
 
-hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s) {
+hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s,
+                           const LaunchTiming &t) {
   const int n_qt = (a.rows + kRows - 1) / kRows;
   const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(kThreads);
   const bool diag = c == StepCase::Diag;
-  if (d == 128) {
-    if (diag) step_f32_kernel<128, true><<<grid, block, 0, s>>>(a);
-    else step_f32_kernel<128, false><<<grid, block, 0, s>>>(a);
-  } else {
-    if (diag) step_f32_kernel<64, true><<<grid, block, 0, s>>>(a);
-    else step_f32_kernel<64, false><<<grid, block, 0, s>>>(a);
-  }
-  return hipGetLastError();
+  void (*kernel)(StepArgs) = d == 128 ? (diag ? step_f32_kernel<128, true> : step_f32_kernel<128, false>)
+                                      : (diag ? step_f32_kernel<64, true> : step_f32_kernel<64, false>);
+  return launch_one(kernel, grid, block, s, t.start, t.stop, a);
 }
 
 }  // namespace ra

@@ -56,6 +56,11 @@ class Event:
         flags = _HIP_EVENT_DISABLE_SYSTEM_FENCE | (0 if timing else _HIP_EVENT_DISABLE_TIMING)
         _check(h.hipEventCreateWithFlags(ctypes.byref(self._ev), flags), "hipEventCreateWithFlags")
 
+    @property
+    def handle(self) -> int:
+        """The hipEvent_t, for the library's timed entry points."""
+        return self._ev.value
+
     def record(self, stream) -> None:
         _check(_runtime().hipEventRecord(self._ev, _handle(stream)), "hipEventRecord")
 

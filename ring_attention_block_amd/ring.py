@@ -82,6 +82,7 @@ class RingEmulator:
         self.ev_ready = [Event(), Event()]
         self.ev_free = [Event(), Event()]
         self.ev_start = Event()
+        self.last_stop = None
 
     def visit(self, order: Sequence[int], source: Callable[[int], tuple],
               fold: Callable[[int, int, tuple], None], drain=None) -> None:
@@ -110,10 +111,17 @@ class RingEmulator:
                 self.ev_ready[nxt_buf].record(copy)
             if cur_buf is not None:
                 self.ev_ready[cur_buf].wait(comp)
+            self.last_stop = None
             fold(s, j, cur)
             if cur_buf is not None:
-                self.ev_free[cur_buf].record(comp)
-                self.ev_free[cur_buf].wait(copy)
+                # The buffer is free once the visit's last kernel has ended: a
+                # timed fold's stop event (bound to that kernel's dispatch)
+                # says so without another marker on the compute stream.
+                if self.last_stop is not None:
+                    self.last_stop.wait(copy)
+                else:
+                    self.ev_free[cur_buf].record(comp)
+                    self.ev_free[cur_buf].wait(copy)
                 if drain is not None:
                     drain(j, cur, copy)
             if nxt_buf is not None:
@@ -125,23 +133,28 @@ class RingEmulator:
             self.ev_start.record(copy)
             self.ev_start.wait(comp)
 
+    def timer_pair(self, case, step_timers, timer_events):
+        """(start, stop) timing events for a launch that step_timers records,
+        or (None, None).  The stop event also marks the end of the visit's
+        compute for the staging protocol (visit)."""
+        if step_timers is None or case == _lib.RA_CASE_SKIP:
+            return None, None
+        if timer_events is not None:
+            e0, e1 = next(timer_events), next(timer_events)
+        else:
+            e0, e1 = Event(timing=True), Event(timing=True)
+        step_timers.append((case, e0, e1))
+        self.last_stop = e1
+        return e0, e1
+
     def step(self, st, q, k, v, i, j, num_blocks, causal, scale, case, step_timers=None,
              timer_events=None, flags=0, out=(None, None)) -> None:
-        """One ra_step (ra_step_ex with flags) on the compute stream, bracketed
-        by timing events when step_timers is given (see run)."""
-        comp = self.compute
-        kw = dict(flags=flags, o_out=out[0], lse_out=out[1])
-        if step_timers is not None and case != _lib.RA_CASE_SKIP:
-            if timer_events is not None:
-                e0, e1 = next(timer_events), next(timer_events)
-            else:
-                e0, e1 = Event(timing=True), Event(timing=True)
-            e0.record(comp)
-            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp, **kw)
-            e1.record(comp)
-            step_timers.append((case, e0, e1))
-        else:
-            _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, comp, **kw)
+        """One ra_step (ra_step_ex with flags) on the compute stream; with
+        step_timers (see run), ra_step_timed binds a pair of timing events to
+        the step kernel's dispatch."""
+        e0, e1 = self.timer_pair(case, step_timers, timer_events)
+        _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, self.compute, flags=flags,
+                  o_out=out[0], lse_out=out[1], start=e0, stop=e1)
 
     def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
             rank: int, num_blocks: int, causal: bool, scale: float,
@@ -203,17 +216,9 @@ class RingEmulator:
 
         def fold(s, j, t):
             case = _lib.step_case(rank, j, num_blocks, causal)
-            comp = self.compute
-            timed = step_timers is not None and case != _lib.RA_CASE_SKIP
-            if timed:
-                e0 = next(timer_events) if timer_events is not None else Event(timing=True)
-                e1 = next(timer_events) if timer_events is not None else Event(timing=True)
-                e0.record(comp)
+            e0, e1 = self.timer_pair(case, step_timers, timer_events)
             _lib.bwd_step(q, dout, lse, delta, t[0], t[1], dq, t[2], t[3], rank, j, num_blocks,
-                          causal, scale, comp)
-            if timed:
-                e1.record(comp)
-                step_timers.append((case, e0, e1))
+                          causal, scale, self.compute, start=e0, stop=e1)
             cases.append(case)
 
         def drain(j, t, stream):
@@ -306,16 +311,10 @@ class ZigzagRing:
         def fold(s, j, t):
             theirs = zigzag_blocks(j, ranks)
             for a, b, case in plan[s][1]:
-                timed = step_timers is not None and case != _lib.RA_CASE_SKIP
-                if timed:
-                    e0 = next(timer_events) if timer_events is not None else Event(timing=True)
-                    e1 = next(timer_events) if timer_events is not None else Event(timing=True)
-                    e0.record(comp)
+                e0, e1 = self.emu.timer_pair(case, step_timers, timer_events)
                 _lib.bwd_step(qs[a], douts[a], lses[a], deltas[a], t[b], t[2 + b], dqs[a],
-                              t[4 + b], t[6 + b], mine[a], theirs[b], 2 * ranks, causal, scale, comp)
-                if timed:
-                    e1.record(comp)
-                    step_timers.append((case, e0, e1))
+                              t[4 + b], t[6 + b], mine[a], theirs[b], 2 * ranks, causal, scale, comp,
+                              start=e0, stop=e1)
 
         def drain(j, t, stream):
             for dst, src in zip(source(j)[4:8], t[4:8]):

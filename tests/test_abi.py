@@ -183,3 +183,40 @@ def test_step_ex_rejects_before_enqueue(L):
     assert ex(3, i=2) == _lib.RA_ERR_INVALID_ARG
     # flags 0 on a skipped block: nothing enqueued, as ra_step
     assert ex(0, i=0, j=1) == _lib.RA_OK
+
+
+def test_timed_entries_reject_before_enqueue(L):
+    # The timed entry points check exactly as their untimed forms; on an error
+    # nothing is enqueued and the events are not touched (invalid handles here).
+    st = _state()
+    bogus = ctypes.c_void_p(FAKE)
+    def timed(flags=0, **kw):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, i=1, j=0, P=2, causal=1, scale=0.125)
+        args.update(kw)
+        return L.ra_step_timed(ctypes.byref(st), args["q"], args["k"], args["v"], _lib.RA_BF16,
+                               st.rows, args["i"], args["j"], args["P"], args["causal"],
+                               args["scale"], flags, FAKE, _lib.RA_F32, FAKE, bogus, bogus, None)
+    assert timed(flags=4) == _lib.RA_ERR_INVALID_ARG
+    assert b"ra_step_timed" in L.ra_last_error() and b"flags" in L.ra_last_error()
+    assert timed(i=2) == _lib.RA_ERR_INVALID_ARG
+    assert timed(q=0) == _lib.RA_ERR_INVALID_ARG
+    assert timed(scale=0.0) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_step_timed(None, FAKE, FAKE, FAKE, _lib.RA_BF16, 128, 1, 0, 2, 1, 0.125, 0, None,
+                           _lib.RA_F32, None, bogus, bogus, None) == _lib.RA_ERR_INVALID_ARG
+    # no events, nothing to fold: OK without any HIP call
+    assert L.ra_step_timed(ctypes.byref(st), FAKE, FAKE, FAKE, _lib.RA_BF16, st.rows, 0, 1, 2, 1,
+                           0.125, 0, None, _lib.RA_F32, None, None, None, None) == _lib.RA_OK
+
+    def bwd(**kw):
+        args = dict(d=128, q=FAKE, i=1, j=0, scale=0.125)
+        args.update(kw)
+        return L.ra_bwd_step_timed(1, 2, 128, args["d"], args["q"], FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   _lib.RA_BF16, FAKE, FAKE, FAKE, args["i"], args["j"], 2, 1,
+                                   args["scale"], bogus, bogus, None)
+    assert bwd(d=96) == _lib.RA_ERR_UNSUPPORTED
+    assert b"ra_bwd_step_timed" in L.ra_last_error()
+    assert bwd(q=FAKE + 4) == _lib.RA_ERR_INVALID_ARG
+    assert bwd(i=3) == _lib.RA_ERR_INVALID_ARG
+    assert bwd(scale=float("nan")) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_bwd_step_timed(1, 2, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, _lib.RA_BF16,
+                               FAKE, FAKE, FAKE, 0, 1, 2, 1, 0.125, None, None, None) == _lib.RA_OK
