@@ -207,11 +207,12 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
  * key/value block from the previous rank into the free buffer ("Ring Attention
  * Paper Breakdown ...", section 2: receive into buffer B while buffer A is
  * computed on, then swap).  Runs as a kernel of this library built to run
- * beside a step: non-temporal loads and stores, and a small grid that leaves
- * the compute units to the step, so a copy alone is slower than a full-chip
- * copy but overlaps well.  bytes == 0 is a no-op; otherwise both pointers must be
- * non-NULL and 16-byte aligned, bytes a multiple of 16, and the ranges must
- * not overlap.
+ * beside a step: non-temporal loads and stores, a small grid that leaves the
+ * compute units to the step, and few registers per wavefront, so that its
+ * wavefronts fit on compute units that also run step workgroups; a copy alone
+ * is slower than a full-chip copy but overlaps well.  bytes == 0 is a no-op;
+ * otherwise both pointers must be non-NULL and 16-byte aligned, bytes a
+ * multiple of 16, and the ranges must not overlap.
  */
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream);
 

@@ -95,13 +95,26 @@ __device__ __forceinline__ int swz(int rho) {
 
 // Workgroup -> (batch*head, tile): consecutive workgroup ids go to different
 // XCDs; when the head count allows, each XCD gets a contiguous range of heads
-// so that the tiles of one head stay in one L2.
-__device__ __forceinline__ void xcd_map(int bid, int n_bh, int n_t, int &bh, int &ti) {
+// so that the tiles of one head stay in one L2.  Within an XCD workgroups
+// start in id order; tile_major (diagonal blocks, whose tiles carry unequal
+// work) walks tile 0 of every head, then tile 1, ..., so the heaviest tiles
+// of all heads start first and the light ones fill in at the end; otherwise
+// one head's tiles follow another's.
+__device__ __forceinline__ void xcd_map(int bid, int n_bh, int n_t, bool tile_major, int &bh,
+                                        int &ti) {
   if ((n_bh & 7) == 0) {
-    const int per_xcd = (n_bh >> 3) * n_t;
-    const int logical = (bid & 7) * per_xcd + (bid >> 3);
-    bh = logical / n_t;
-    ti = logical % n_t;
+    const int heads8 = n_bh >> 3, k = bid >> 3, x = bid & 7;
+    if (tile_major) {
+      bh = x * heads8 + k % heads8;
+      ti = k / heads8;
+    } else {
+      const int logical = x * heads8 * n_t + k;
+      bh = logical / n_t;
+      ti = logical % n_t;
+    }
+  } else if (tile_major) {
+    bh = bid % n_bh;
+    ti = bid / n_bh;
   } else {
     bh = bid / n_t;
     ti = bid % n_t;
@@ -267,7 +280,7 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
   const int rows = a.rows;
   const int n_qt = (rows + kBM - 1) / kBM;
   int bh, qi;
-  xcd_map(blockIdx.x, a.bh, n_qt, bh, qi);
+  xcd_map(blockIdx.x, a.bh, n_qt, kDiag, bh, qi);
   const int qt = kDiag ? n_qt - 1 - qi : qi;   // diagonal: heaviest query tiles first
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -432,7 +445,7 @@ __global__ void __launch_bounds__(64 * kWaves, D == 128 ? 1 : 2) bwd_dkdv_bf16_k
   const int rows = a.rows;
   const int n_kt = (rows + kBK - 1) / kBK;
   int bh, kt;
-  xcd_map(blockIdx.x, a.bh, n_kt, bh, kt);   // diagonal: low keys (most queries) first
+  xcd_map(blockIdx.x, a.bh, n_kt, kDiag, bh, kt);   // diagonal: low keys (most queries) first
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, h = lane >> 5;

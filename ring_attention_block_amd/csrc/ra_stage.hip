@@ -4,11 +4,19 @@
 // Near-Infinite Context", section 2: receive into buffer B, then swap).
 //
 // The copy runs beside a step kernel, which it should disturb as little as
-// possible: the loads and stores carry the non-temporal hint (the block is not
-// reused from cache by this copy), and the grid is small (kMaxBlocks
-// workgroups of four wavefronts: one on half of the CUs), so the step kernel's
-// workgroups, which need most of a CU each, still find room on every CU.  The copy then takes a few tens of microseconds for a 32 MiB block,
-// well inside one step.
+// possible:
+//   * a small grid (kMaxBlocks workgroups of four wavefronts, each copying one
+//     contiguous chunk), so the step kernel keeps the compute units;
+//   * few registers: buffer loads and stores address the chunk through a
+//     32-bit lane offset plus a scalar offset per unrolled access, so a
+//     wavefront holds kUnroll 16-byte values and one offset (15 VGPRs, 16
+//     allocated).  Two wavefronts of the forward step kernel's full-block
+//     (8-wavefront) or diagonal variant at head_dim 128 leave at least 16 of
+//     the 512 registers per lane of a SIMD free, so a copy wavefront fits
+//     beside them instead of taking the place of a step workgroup;
+//   * non-temporal loads and stores (the block is not reused from cache by
+//     this copy).
+// A 32 MiB block then takes a few tens of microseconds, well inside one step.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,42 +28,54 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 3;
 constexpr int64_t kMaxBlocks = 128;
+constexpr int64_t kMaxChunk = (int64_t)1 << 30;   // buffer offsets are 32-bit
+constexpr int kNonTemporal = 2;                    // buffer access cache policy: nt
+constexpr int kRawBuffer = 0x00020000;             // buffer resource: raw (untyped) 32-bit words
 
-template <bool kNonTemporal>
-__global__ void __launch_bounds__(kThreads) stage_copy_kernel(u32x4 *__restrict__ dst,
-                                                              const u32x4 *__restrict__ src,
-                                                              int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+// Workgroup b copies bytes [b * chunk, min((b + 1) * chunk, bytes)) of src to
+// dst; chunk and bytes are multiples of 16.  The buffer range check keeps
+// every access inside the chunk.
+__global__ void __launch_bounds__(kThreads) stage_copy_kernel(char *__restrict__ dst,
+                                                              const char *__restrict__ src,
+                                                              int64_t bytes, int64_t chunk) {
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  if (c0 >= bytes) return;
+  const uint32_t len = (uint32_t)(bytes - c0 < chunk ? bytes - c0 : chunk);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(src) + c0, 0, len, kRawBuffer);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst + c0, 0, len, kRawBuffer);
+  constexpr uint32_t kStep = kThreads * 16;
+  uint32_t off = threadIdx.x * 16;
+  for (; off + (kUnroll - 1) * kStep < len; off += kUnroll * kStep) {
     u32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      v[u] = kNonTemporal ? __builtin_nontemporal_load(src + i + u * stride) : src[i + u * stride];
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, u * kStep, kNonTemporal);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (kNonTemporal) __builtin_nontemporal_store(v[u], dst + i + u * stride);
-      else dst[i + u * stride] = v[u];
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, off, u * kStep, kNonTemporal);
   }
-  for (; i < n16; i += stride) {
-    const u32x4 v = kNonTemporal ? __builtin_nontemporal_load(src + i) : src[i];
-    if (kNonTemporal) __builtin_nontemporal_store(v, dst + i);
-    else dst[i] = v;
+  for (; off < len; off += kStep) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, off, 0, kNonTemporal);
   }
 }
 
 }  // namespace
 
 hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
-  const int64_t n16 = (int64_t)(bytes / 16);
-  int64_t blocks = (n16 + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+  const int64_t n = (int64_t)bytes;
+  constexpr int64_t kPerRound = (int64_t)kThreads * 16 * kUnroll;
+  int64_t blocks = (n + kPerRound - 1) / kPerRound;
   if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  const int64_t min_blocks = (n + kMaxChunk - 1) / kMaxChunk;
+  if (blocks < min_blocks) blocks = min_blocks;
   if (blocks < 1) blocks = 1;
-  stage_copy_kernel<true><<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
-      static_cast<u32x4 *>(dst), static_cast<const u32x4 *>(src), n16);
+  const int64_t chunk = ((n + blocks - 1) / blocks + 15) & ~(int64_t)15;
+  stage_copy_kernel<<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(
+      static_cast<char *>(dst), static_cast<const char *>(src), n, chunk);
   return hipGetLastError();
 }
 

@@ -264,21 +264,33 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   const int n_qt = (rows + kBM - 1) / kBM;
   // Workgroup -> (head, query tile).  Consecutive workgroup ids go to
   // different XCDs; when the head count allows, give each XCD a contiguous
-  // range of heads so that one head's key/value tiles stay in one L2.
+  // range of heads so that one head's key/value tiles stay in one L2.  Within
+  // an XCD, workgroups start in id order: full blocks walk one head's tiles
+  // after another; diagonal blocks, whose tiles carry unequal work, walk the
+  // tiles of all the XCD's heads from the heaviest down (largest work first,
+  // so the light tiles fill in at the end).
   int bh, qi;
   {
     const int bid = blockIdx.x;
     if ((a.bh & 7) == 0) {
-      const int per_xcd = (a.bh >> 3) * n_qt;
-      const int logical = (bid & 7) * per_xcd + (bid >> 3);
-      bh = logical / n_qt;
-      qi = logical % n_qt;
+      const int heads8 = a.bh >> 3, k = bid >> 3, x = bid & 7;
+      if (kDiag) {
+        bh = x * heads8 + k % heads8;
+        qi = k / heads8;
+      } else {
+        const int logical = x * heads8 * n_qt + k;
+        bh = logical / n_qt;
+        qi = logical % n_qt;
+      }
+    } else if (kDiag) {
+      bh = bid % a.bh;
+      qi = bid / a.bh;
     } else {
       bh = bid / n_qt;
       qi = bid % n_qt;
     }
   }
-  // Diagonal blocks: heaviest query tiles first.
+  // Diagonal blocks: qi 0 is the heaviest query tile (the last one).
   const int qt = kDiag ? n_qt - 1 - qi : qi;
 
   const int tid = threadIdx.x;
