@@ -73,6 +73,11 @@ BWD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                    "ra_bwd_step_bf16_full_causal_h32_d128_c4096_hbm_traffic.md")
 
 
+def timed_rings(args) -> int:
+    """Timed rings whose step launches carry timing events (every time_every-th)."""
+    return (args.steps + args.time_every - 1) // args.time_every
+
+
 def measured_traffic(wl, profile=TRAFFIC_PROFILE):
     """HBM bytes per full-step launch from a committed FETCH_SIZE/WRITE_SIZE summary.
 
@@ -257,11 +262,11 @@ def bench_backward(args, wl, rank):
         one_ring()
     torch.cuda.synchronize()
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
-    pool = iter([Event(timing=True) for _ in range(2 * launched * args.steps)])
+    pool = iter([Event(timing=True) for _ in range(2 * launched * timed_rings(args))])
     timers = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_ring(timers, pool)
+    for r in range(args.steps):
+        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
@@ -299,6 +304,7 @@ def bench_backward(args, wl, rank):
                                  if full and not zigzag else None),
                      "avg_launch_ms": round(dom_ms, 5),
                      "launches": len(full) if full else len(diag),
+                     "timed_rings": f"1 in {args.time_every} of the {args.steps} timed rings",
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
     }
     print(json.dumps(line), flush=True)
@@ -311,6 +317,10 @@ def main():
     # 30 untimed rings: with 3 the clocks have not settled and the timed
     # rings of the 32-head causal workload ran 1-2% slower.
     ap.add_argument("--warmup", type=int, default=30)
+    # Each timing event costs the compute stream a few microseconds between two
+    # step kernels, so the kernel durations are sampled: the launches of every
+    # K-th timed ring carry events (all rings with K = 1).
+    ap.add_argument("--time-every", type=int, default=4)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--partition", default="contiguous", choices=("contiguous", "zigzag"),
@@ -328,6 +338,8 @@ def main():
                          "first and last ring steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
+    if args.time_every < 1:
+        ap.error("--time-every must be >= 1")
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring of one rank is emulated on a "
@@ -425,14 +437,14 @@ def main():
         one_ring()
     torch.cuda.synchronize()
 
-    # Timing events for every launched step of the timed rings, created
-    # before the timed region.
+    # Timing events for every launched step of the sampled timed rings,
+    # created before the timed region.
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
-    pool = iter([Event(timing=True) for _ in range(2 * launched * args.steps)])
+    pool = iter([Event(timing=True) for _ in range(2 * launched * timed_rings(args))])
     timers = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_ring(timers, pool)
+    for r in range(args.steps):
+        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -477,6 +489,7 @@ def main():
                                  else None),
                      "avg_launch_ms": round(dom_ms, 5),
                      "launches": len(full) if full else len(diag),
+                     "timed_rings": f"1 in {args.time_every} of the {args.steps} timed rings",
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
     }
     if not args.no_cpu_baseline:

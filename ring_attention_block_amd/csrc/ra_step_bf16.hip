@@ -525,14 +525,14 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     }
     if (t < n_tiles) iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
   } else {
-    // head_dim 64: the tiles before the first one that needs the element mask
-    // (on the diagonal: keys before every row of the wavefront) run the
-    // interleaved block as long as the following tile needs no mask either;
-    // the rest the masked one.  Every wavefront runs n_tiles iterations with
-    // one barrier each, whichever block it takes.  (At head_dim 128 the two
-    // blocks in one kernel leave too few registers, and the masked block alone
-    // is faster.)
-    if constexpr (D == 64) {
+    // head_dim 64, and 8-wavefront workgroups: the tiles before the first one
+    // that needs the element mask (on the diagonal: keys before every row of
+    // the wavefront) run the interleaved block as long as the following tile
+    // needs no mask either; the rest the masked one.  Every wavefront runs n_tiles iterations with
+    // one barrier each, whichever block it takes.  (At head_dim 128 with four
+    // wavefronts per workgroup the two blocks in one kernel leave too few
+    // registers, and the masked block alone is faster; with eight they fit.)
+    if constexpr (D == 64 || kW == 8) {
       const int first_diag = kDiag ? (q0w >= kBN - 1 ? (q0w - (kBN - 1)) / kBN + 1 : 0) : n_tiles;
       const int first_tail = kv_rows >= kBN ? (kv_rows - kBN) / kBN + 1 : 0;
       const int n_fast = max(0, min(min(first_diag, first_tail) - 1, n_tiles - 1));
@@ -630,15 +630,18 @@ hipError_t launch(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
 // tile), unless that gives fewer workgroups than the chip has compute units
 // (256 on MI355X); then 4-wavefront workgroups, twice as many (measured at 8
 // heads x 2048 rows: 35 us against 50 us; at 32 heads x 4096 rows the
-// 8-wavefront grid is faster).  Diagonal blocks: 4-wavefront workgroups,
-// whose finer query tiles waste less work on the masked triangle and balance
-// better.
+// 8-wavefront grid is faster).  Diagonal blocks at head_dim 128: 8-wavefront
+// workgroups, which have the registers to run their tiles before the diagonal
+// through the interleaved block (32 heads x 4096 rows: 137 us against 153 us
+// with 4-wavefront workgroups, which must take the masked block throughout);
+// at head_dim 64: 4-wavefront workgroups, whose finer query tiles waste less
+// work on the masked triangle.
 constexpr int64_t kComputeUnits = 256;
 
 template <int D, bool kDiag>
 hipError_t launch_d(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
   if constexpr (kDiag) {
-    return launch<D, kDiag, 4>(a, s, t);
+    return launch<D, kDiag, D == 128 ? 8 : 4>(a, s, t);
   } else {
     if ((int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s, t);
     return launch<D, kDiag, 8>(a, s, t);
