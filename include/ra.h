@@ -50,7 +50,8 @@ typedef enum {
   RA_OK = 0,
   RA_ERR_INVALID_ARG = -1,  /* bad shape, index, pointer, alignment or scale   */
   RA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, kv_rows,
-                               bf16 blocks over 2^31 bytes per (batch, head)) */
+                               bf16 blocks of 2^31 bytes or more per
+                               (batch, head)) */
   RA_ERR_HIP = -3           /* HIP refused to enqueue a kernel or copy         */
 } ra_status;
 
@@ -127,8 +128,9 @@ int32_t ra_step_case(int32_t q_block, int32_t kv_block, int32_t num_blocks, int3
  *              positions are q_block*rows + r and kv_block*rows + t.
  *   scale      score multiplier, finite and > 0 (1/sqrt(head_dim) normally).
  * bf16 inputs use the MFMA path (fp32 accumulation, P rounded to bf16 before
- * the P V product) and are limited to 2^31 bytes per (batch, head) block of
- * q, k or v (else RA_ERR_UNSUPPORTED); f32 inputs use an fp32 path.  A skipped block returns
+ * the P V product) and must stay below 2^31 bytes per (batch, head) block of
+ * q, k or v (else RA_ERR_UNSUPPORTED; the fp32 O state of such a block then
+ * stays below 2^32 bytes); f32 inputs use an fp32 path.  A skipped block returns
  * RA_OK and enqueues nothing, leaving the state bit-identical.
  */
 ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_dtype in_dtype,

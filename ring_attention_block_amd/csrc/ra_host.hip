@@ -67,10 +67,10 @@ ra_status check_state(const ra_state *st, const char *name, int64_t *n_rows) {
   return RA_OK;
 }
 
-// The bf16 kernels address a (batch, head) block through a buffer resource
-// whose byte range and offsets are 32-bit.
+// The bf16 kernels address a (batch, head) block, and its fp32 O state (twice
+// the bytes), through buffer resources whose byte range and offsets are 32-bit.
 bool bf16_block_too_long(int64_t rows, int32_t head_dim) {
-  return rows * head_dim * 2 > ((int64_t)1 << 31);
+  return rows * head_dim * 2 >= ((int64_t)1 << 31);
 }
 
 ra_status hip_status(hipError_t e, const char *what) {
@@ -141,7 +141,7 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   if ((int64_t)st->batch * st->heads * kv_rows > ((int64_t)1 << 40) / st->head_dim)
     return fail(RA_ERR_INVALID_ARG, "%s: key/value block of %d rows is too large", name, kv_rows);
   if (in_dtype == RA_BF16 && bf16_block_too_long(st->rows > kv_rows ? st->rows : kv_rows, st->head_dim))
-    return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks are limited to 2^31 bytes per (batch, head)", name);
+    return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks must stay below 2^31 bytes per (batch, head)", name);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(RA_ERR_INVALID_ARG, "%s: scale=%g must be finite and > 0", name, (double)scale);
   if (flags & ~(uint32_t)(RA_STEP_FRESH | RA_STEP_FINALIZE))
@@ -301,7 +301,7 @@ static ra_status bwd_impl(const char *name, int32_t batch, int32_t heads, int32_
   if (in_dtype != RA_F32 && in_dtype != RA_BF16)
     return fail(RA_ERR_INVALID_ARG, "%s: in_dtype=%d is not RA_F32 or RA_BF16", name, (int)in_dtype);
   if (in_dtype == RA_BF16 && bf16_block_too_long(rows, head_dim))
-    return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks are limited to 2^31 bytes per (batch, head)", name);
+    return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks must stay below 2^31 bytes per (batch, head)", name);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(RA_ERR_INVALID_ARG, "%s: scale=%g must be finite and > 0", name, (double)scale);
   if (n > 0) {

@@ -56,6 +56,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -304,6 +305,16 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   const size_t kv_base = (size_t)bh * kv_rows * D;
   const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.q) + base;
   float *__restrict__ O = a.o + base;
+  // The query rows and the state are read through buffer resources whose
+  // range check returns 0 past the block end and, for the state, for every row
+  // of a fresh step.  The loads then need no branch (a load under a branch is
+  // waited for inside it, which serialised them).
+  const bool fresh = (a.flags & kStepFresh) != 0;
+  const uint32_t state_rows = fresh ? 0u : (uint32_t)rows;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q, (uint32_t)rows * T::kRowBytes);
+  const __amdgpu_buffer_rsrc_t rso = make_rsrc(O, state_rows * (uint32_t)(D * 4));
+  const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a.m + (size_t)bh * rows, state_rows * 4u);
+  const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.l + (size_t)bh * rows, state_rows * 4u);
   const uint32_t blk_bytes = (uint32_t)kv_rows * T::kRowBytes;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t *>(a.k) + kv_base, blk_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t *>(a.v) + kv_base, blk_bytes);
@@ -331,19 +342,18 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   f32x16 oacc[kDB];
   RowState rs;
   {
-    const size_t ro = (size_t)row * D;
 #pragma unroll
     for (int c = 0; c < kQK; ++c) {
-      uint4 u = row_ok ? *reinterpret_cast<const uint4 *>(Q + ro + c * 16 + h * 8)
-                       : make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, u);
+      const uint32_t off = (uint32_t)row * T::kRowBytes + (uint32_t)(c * 16 + h * 8) * 2;
+      qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
-    const size_t sr = (size_t)bh * rows + row;
-    const bool read_state = row_ok && !(a.flags & kStepFresh);
-    const float m_state = read_state ? a.m[sr] * kLog2e : -INFINITY;
+    const float m_ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsm, (uint32_t)row * 4, 0, 0));
+    const float l_ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, (uint32_t)row * 4, 0, 0));
+    const bool read_state = row_ok && !fresh;
+    const float m_state = read_state ? m_ld * kLog2e : -INFINITY;
     rs.m_ref = m_state;
     rs.m_run = m_state;
-    rs.l = (read_state && h == 0) ? a.l[sr] : 0.f;
+    rs.l = (read_state && h == 0) ? l_ld : 0.f;
   }
 
   // Per-lane LDS byte offsets of the fragments within a tile buffer.
@@ -416,18 +426,16 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // its loads are issued only now, so the first barrier does not wait for
   // them and they overlap the first scores.
   {
-    const size_t ro = (size_t)row * D;
-    const bool read_o = row_ok && !(a.flags & kStepFresh);
 #pragma unroll
     for (int b = 0; b < kDB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float4 x = read_o ? *reinterpret_cast<const float4 *>(O + ro + b * 32 + g * 8 + h * 4)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-        oacc[b][4 * g + 0] = x.x;
-        oacc[b][4 * g + 1] = x.y;
-        oacc[b][4 * g + 2] = x.z;
-        oacc[b][4 * g + 3] = x.w;
+        const uint32_t off = ((uint32_t)row * D + (uint32_t)(b * 32 + g * 8 + h * 4)) * 4;
+        // (Cast the whole vector: a scalar bit cast of one element of the
+        // loaded vector was compiled as a cast of element 0.)
+        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rso, off, 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[b][4 * g + e] = x[e];
       }
   }
   // kIdle: some wavefront's rows may all lie past the block end (a short
@@ -518,12 +526,17 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   using Masked = std::integral_constant<bool, false>;
   int t = 0;
   if constexpr (!kMask) {
+    // Iteration 0 runs outside the loop, so that the O-state loads issued
+    // after the first barrier are first waited for at its P V product rather
+    // than before the loop (n_tiles >= 1: empty blocks launch nothing).
+    iteration(Fast{}, 0, lds_k0, lds_v1, lds_k1, lds_v0);
+    t = 1;
 #pragma clang loop unroll(disable)
     for (; t + 1 < n_tiles; t += 2) {
-      iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
-      iteration(Fast{}, t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
+      iteration(Fast{}, t, lds_k1, lds_v0, lds_k0, lds_v1);
+      iteration(Fast{}, t + 1, lds_k0, lds_v1, lds_k1, lds_v0);
     }
-    if (t < n_tiles) iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+    if (t < n_tiles) iteration(Fast{}, t, lds_k1, lds_v0, lds_k0, lds_v1);
   } else {
     // head_dim 64, and 8-wavefront workgroups: the tiles before the first one
     // that needs the element mask (on the diagonal: keys before every row of

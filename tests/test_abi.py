@@ -91,8 +91,8 @@ def test_step_rejects_before_enqueue(L):
     assert _step(L, st, q=0) == _lib.RA_ERR_INVALID_ARG
     assert _step(L, st, v=FAKE + 8) == _lib.RA_ERR_INVALID_ARG
     assert b"aligned" in L.ra_last_error()
-    # bf16 blocks: at most 2^31 bytes per (batch, head)
-    assert _step(L, _state(rows=(1 << 23) + 1)) == _lib.RA_ERR_UNSUPPORTED
+    # bf16 blocks: below 2^31 bytes per (batch, head) (head_dim 128: fewer than 2^23 rows)
+    assert _step(L, _state(rows=1 << 23)) == _lib.RA_ERR_UNSUPPORTED
     assert b"2^31" in L.ra_last_error()
     assert _step(L, _state(m=0)) == _lib.RA_ERR_INVALID_ARG
     assert _step(L, _state(o=FAKE + 4)) == _lib.RA_ERR_INVALID_ARG
@@ -143,7 +143,7 @@ def test_bwd_rejects_before_enqueue(L):
     assert _bwd(L, i=2, P=2) == _lib.RA_ERR_INVALID_ARG
     assert _bwd(L, causal=2) == _lib.RA_ERR_INVALID_ARG
     assert _bwd(L, dtype=9) == _lib.RA_ERR_INVALID_ARG
-    assert _bwd(L, rows=(1 << 23) + 1) == _lib.RA_ERR_UNSUPPORTED
+    assert _bwd(L, rows=1 << 23) == _lib.RA_ERR_UNSUPPORTED
     for bad in (0.0, -0.5, float("inf"), float("nan")):
         assert _bwd(L, scale=bad) == _lib.RA_ERR_INVALID_ARG
     for name in ("q", "dout", "lse", "delta", "k", "v", "dq", "dk", "dv"):
