@@ -304,22 +304,26 @@ __global__ void __launch_bounds__(64 * kWaves, 2) bwd_dq_bf16_kernel(BwdArgs a) 
   issue_copy<D>(lds_v0, rv, coff, 0, wave);
 
   // B operands: lane (r, h) holds q[row][16c + 8h ..] and do[row][16c + 8h ..].
+  // Rows, LSE and D come through range-checked buffer loads (0 past the block
+  // end), so no load sits under a branch (each would be waited for inside it)
+  // and none is a flat access (which waits for the LDS copies before it).
   bf16x8 qf[kQK], of[kQK];
-  float nl2 = -INFINITY, dd = 0.f;
+  float nl2, dd;
   {
-    const uint16_t *Q = static_cast<const uint16_t *>(a.q) + base + (size_t)row * D;
-    const uint16_t *dO = static_cast<const uint16_t *>(a.dout) + base + (size_t)row * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const uint16_t *>(a.q) + base, blk_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<const uint16_t *>(a.dout) + base, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + (size_t)bh * rows, (uint32_t)rows * 4u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + (size_t)bh * rows, (uint32_t)rows * 4u);
 #pragma unroll
     for (int c = 0; c < kQK; ++c) {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, row_ok ? *reinterpret_cast<const uint4 *>(Q + c * 16 + h * 8) : z);
-      of[c] = __builtin_bit_cast(bf16x8, row_ok ? *reinterpret_cast<const uint4 *>(dO + c * 16 + h * 8) : z);
+      const uint32_t off = (uint32_t)row * T::kRowBytes + (uint32_t)(c * 16 + h * 8) * 2;
+      qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      of[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ro, off, 0, 0));
     }
-    if (row_ok) {
-      const size_t sr = (size_t)bh * rows + row;
-      nl2 = neg_lse2(a.lse[sr]);
-      dd = a.delta[sr];
-    }
+    const float lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)row * 4, 0, 0));
+    const float del = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)row * 4, 0, 0));
+    nl2 = row_ok ? neg_lse2(lse) : -INFINITY;
+    dd = row_ok ? del : 0.f;
   }
   f32x16 dq[kDB];
 #pragma unroll
