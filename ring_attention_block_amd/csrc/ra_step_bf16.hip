@@ -646,15 +646,18 @@ hipError_t launch(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
 // 8-wavefront grid is faster).  Diagonal blocks at head_dim 128: 8-wavefront
 // workgroups, which have the registers to run their tiles before the diagonal
 // through the interleaved block (32 heads x 4096 rows: 137 us against 153 us
-// with 4-wavefront workgroups, which must take the masked block throughout);
-// at head_dim 64: 4-wavefront workgroups, whose finer query tiles waste less
-// work on the masked triangle.
+// with 4-wavefront workgroups, which must take the masked block throughout),
+// unless that grid leaves compute units idle as above (8 heads x 2048 rows:
+// 43 us with 4-wavefront workgroups against 49 us); at head_dim 64:
+// 4-wavefront workgroups, whose finer query tiles waste less work on the
+// masked triangle.
 constexpr int64_t kComputeUnits = 256;
 
 template <int D, bool kDiag>
 hipError_t launch_d(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
   if constexpr (kDiag) {
-    return launch<D, kDiag, D == 128 ? 8 : 4>(a, s, t);
+    if (D == 64 || (int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s, t);
+    return launch<D, kDiag, 8>(a, s, t);
   } else {
     if ((int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s, t);
     return launch<D, kDiag, 8>(a, s, t);
