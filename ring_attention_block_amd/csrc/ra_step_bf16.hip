@@ -341,20 +341,14 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   // O^T accumulators: block b, entry i <-> column 32b + 8(i/4) + 4h + i%4.
   f32x16 oacc[kDB];
   RowState rs;
-  {
 #pragma unroll
-    for (int c = 0; c < kQK; ++c) {
-      const uint32_t off = (uint32_t)row * T::kRowBytes + (uint32_t)(c * 16 + h * 8) * 2;
-      qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    }
-    const float m_ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsm, (uint32_t)row * 4, 0, 0));
-    const float l_ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, (uint32_t)row * 4, 0, 0));
-    const bool read_state = row_ok && !fresh;
-    const float m_state = read_state ? m_ld * kLog2e : -INFINITY;
-    rs.m_ref = m_state;
-    rs.m_run = m_state;
-    rs.l = (read_state && h == 0) ? l_ld : 0.f;
+  for (int c = 0; c < kQK; ++c) {
+    const uint32_t off = (uint32_t)row * T::kRowBytes + (uint32_t)(c * 16 + h * 8) * 2;
+    qf[c] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
   }
+  // m and l are used only after the first barrier (below).
+  const float m_ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsm, (uint32_t)row * 4, 0, 0));
+  const float l_ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsl, (uint32_t)row * 4, 0, 0));
 
   // Per-lane LDS byte offsets of the fragments within a tile buffer.
   //   K fragment (sb, c): row 32sb + r, chunk (2c + h) swizzled by the row.
@@ -414,17 +408,11 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     return (kDiag && t * kBN + kBN - 1 > q0w) || (t * kBN + kBN > kv_rows);
   };
 
-  // Software pipeline, one tile ahead.  Iteration t issues the copies of
-  // K(t+2) and V(t+1), and in one branch-free block computes the scores of
-  // tile t+1, the exponentials of tile t, the P V product of tile t and the
-  // row maximum of tile t+1; the rare rescale of O for tile t+1 follows.
-  // K(t+2) reuses the buffer of K(t), read one iteration earlier; V(t+1)
-  // reuses that of V(t-1).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();   // K(0), V(0), K(1) (and a zeroed tail) visible to all
-  // The O state is first needed by the P V product of tile 0 (or a rescale):
-  // its loads are issued only now, so the first barrier does not wait for
-  // them and they overlap the first scores.
+  // The O-state loads are issued last, before the first barrier, which waits
+  // only for the copies and the loads issued before them (vmcnt counts in
+  // issue order); they are first waited for at the P V product of tile 0.
+  // The scheduling barrier keeps every earlier load ahead of them.
+  __builtin_amdgcn_sched_barrier(0);
   {
 #pragma unroll
     for (int b = 0; b < kDB; ++b)
@@ -438,6 +426,22 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
         for (int e = 0; e < 4; ++e) oacc[b][4 * g + e] = x[e];
       }
   }
+  constexpr int kOLoads = kDB * 4;
+  __builtin_amdgcn_s_waitcnt((kOLoads & 15) | ((kOLoads >> 4) << 14) | (7 << 4));  // vmcnt(kOLoads) lgkmcnt(0)
+  __syncthreads();   // K(0), V(0), K(1) (and a zeroed tail) visible to all
+  {
+    const bool read_state = row_ok && !fresh;
+    const float m_state = read_state ? m_ld * kLog2e : -INFINITY;
+    rs.m_ref = m_state;
+    rs.m_run = m_state;
+    rs.l = (read_state && h == 0) ? l_ld : 0.f;
+  }
+  // Software pipeline, one tile ahead.  Iteration t issues the copies of
+  // K(t+2) and V(t+1), and in one branch-free block computes the scores of
+  // tile t+1, the exponentials of tile t, the P V product of tile t and the
+  // row maximum of tile t+1; the rare rescale of O for tile t+1 follows.
+  // K(t+2) reuses the buffer of K(t), read one iteration earlier; V(t+1)
+  // reuses that of V(t-1).
   // kIdle: some wavefront's rows may all lie past the block end (a short
   // query block, as in decoding); such a wavefront only issues its share of
   // the copies and takes the barriers.  Without kIdle the test compiles away
