@@ -204,6 +204,28 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
                       hipStream_t stream);
 
 /*
+ * Reduce partial states and finalize in one pass: the global online-softmax
+ * reduction of decoding against a sharded key/value cache ("Ring Attention：
+ * 把超长序列沿设备环流动", section "训练与推理的适用方式不同": each shard
+ * holder folds the broadcast query block into a partial state, then the
+ * partial states are combined), followed by ra_finalize.  The state holds
+ * batch = out_batch * parts partial states: state batch b * parts + p is part
+ * p of output batch b, each over a disjoint key set.  Per row, with
+ * m = max_p m_p and w_p = exp(m_p - m) (w_p = 0 for a part whose m_p is -inf,
+ * i.e. that saw no key), l = sum_p w_p l_p and
+ *   o_out   [out_batch, heads, rows, head_dim] in out_dtype (RA_F32 or
+ *           RA_BF16, round to nearest even) = (sum_p w_p o_p) / l; may be
+ *           NULL to skip.
+ *   lse_out [out_batch, heads, rows] fp32 = m + ln l; may be NULL to skip.
+ * The same result as merging the parts pairwise with ra_lse_merge (any
+ * order) and finalizing, up to rounding.  A row no part saw gives o_out = 0
+ * and lse_out = -inf.  parts must divide batch (RA_ERR_INVALID_ARG
+ * otherwise); outputs 16-byte aligned.  The state is not modified.
+ */
+ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_dtype out_dtype,
+                            float *lse_out, hipStream_t stream);
+
+/*
  * Stage a block: asynchronous device-to-device copy of `bytes` bytes from src
  * to dst on `stream`.  On one GPU this stands in for the receive of the next
  * key/value block from the previous rank into the free buffer ("Ring Attention

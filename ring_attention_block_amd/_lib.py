@@ -20,7 +20,7 @@ RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
 
 # Every symbol include/ra.h declares.
 EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_step_timed", "ra_lse_merge",
-           "ra_finalize", "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_bwd_step_timed",
+           "ra_finalize", "ra_merge_finalize", "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_bwd_step_timed",
            "ra_status_string", "ra_last_error")
 
 
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
                                              f32, ctypes.c_uint32, vp, ctypes.c_int, vp, vp, vp, vp]),
             "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
+            "ra_merge_finalize": (ctypes.c_int, [sp, i32, vp, ctypes.c_int, vp, vp]),
             "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
             "ra_bwd_prepare": (ctypes.c_int, [i32, i32, i32, i32, vp, ctypes.c_int, vp, ctypes.c_int,
                                               vp, vp]),
@@ -218,6 +219,28 @@ def finalize(st: State, out_dtype=torch.float32, stream=None, o_out=None, lse_ou
     if o_out.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"unsupported output dtype {o_out.dtype}")
     _check(lib().ra_finalize(ctypes.byref(st.c), _ptr(o_out), code, _ptr(lse_out), _stream(stream)))
+    return o_out, lse_out
+
+
+def merge_finalize(st: State, parts: int, out_dtype=torch.float32, stream=None, o_out=None,
+                   lse_out=None):
+    """Reduce the `parts` partial states of each output batch (state batches
+    b*parts .. b*parts+parts-1) and finalize.  Returns (O [B/parts,H,rows,d]
+    in out_dtype, LSE [B/parts,H,rows] fp32)."""
+    b, h, r, d = st.shape
+    if parts < 1 or b % parts:
+        raise ValueError(f"parts={parts} must divide the state batch {b}")
+    if o_out is None:
+        o_out = torch.empty((b // parts, h, r, d), dtype=out_dtype, device=st.o.device)
+    if lse_out is None:
+        lse_out = torch.empty((b // parts, h, r), dtype=torch.float32, device=st.o.device)
+    if o_out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"unsupported output dtype {o_out.dtype}")
+    if tuple(o_out.shape) != (b // parts, h, r, d) or tuple(lse_out.shape) != (b // parts, h, r):
+        raise ValueError("merge_finalize: output shapes do not match the state")
+    code = RA_BF16 if o_out.dtype == torch.bfloat16 else RA_F32
+    _check(lib().ra_merge_finalize(ctypes.byref(st.c), int(parts), _ptr(o_out), code, _ptr(lse_out),
+                                   _stream(stream)))
     return o_out, lse_out
 
 

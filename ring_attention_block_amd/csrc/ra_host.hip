@@ -269,6 +269,27 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
                     "ra_finalize launch");
 }
 
+ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_dtype out_dtype,
+                            float *lse_out, hipStream_t stream) {
+  int64_t n = 0;
+  ra_status s = check_state(st, "ra_merge_finalize", &n);
+  if (s != RA_OK) return s;
+  if (out_dtype != RA_F32 && out_dtype != RA_BF16)
+    return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: out_dtype=%d is not RA_F32 or RA_BF16",
+                (int)out_dtype);
+  if (parts < 1 || st->batch % parts != 0)
+    return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: parts=%d must be >= 1 and divide batch=%d",
+                (int)parts, (int)st->batch);
+  if (n == 0 || (!o_out && !lse_out)) return ok();
+  if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
+    return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: outputs must be 16-byte aligned");
+  const int64_t hr = (int64_t)st->heads * st->rows;
+  (void)hipGetLastError();
+  return hip_status(ra::launch_merge_finalize(st->m, st->l, st->o, o_out, out_dtype == RA_BF16,
+                                              lse_out, n / parts, hr, parts, st->head_dim, stream),
+                    "ra_merge_finalize launch");
+}
+
 ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
                          const void *o, ra_dtype o_dtype, const void *dout, ra_dtype do_dtype,
                          float *delta, hipStream_t stream) {

@@ -69,6 +69,11 @@ hipError_t launch_state_merge(float *dm, float *dl, float *dO, const float *sm, 
                               const float *sO, int64_t n_rows, int d, hipStream_t s);
 hipError_t launch_finalize(const float *m, const float *l, const float *o, void *o_out,
                            bool out_bf16, float *lse, int64_t n_rows, int d, hipStream_t s);
+// Reduce `parts` partial states per output row (state batches b*parts + p of
+// output batch b) and finalize; hr = heads * rows.
+hipError_t launch_merge_finalize(const float *m, const float *l, const float *o, void *o_out,
+                                 bool out_bf16, float *lse, int64_t n_out_rows, int64_t hr,
+                                 int parts, int d, hipStream_t s);
 hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s,
                             const LaunchTiming &t = {});
 hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s,

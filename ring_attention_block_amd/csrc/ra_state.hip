@@ -101,6 +101,54 @@ __global__ void __launch_bounds__(kThreads) finalize_kernel(
   if (lse && chunk == 0) lse[row] = lr > 0.f ? m[row] + logf(lr) : -INFINITY;
 }
 
+// The reduction of partial states over disjoint key sets, finalized: for each
+// output row the parts p = 0 .. parts-1 (state batches b*parts + p of output
+// batch b) give m = max_p m_p, w_p = exp(m_p - m) (0 for a part that saw no
+// key: exp(-inf - -inf) is never formed), l = sum_p w_p l_p,
+// out = (sum_p w_p O_p) / l and lse = m + ln l; a row no part saw gives 0 and
+// -inf.  hr = heads * rows (rows of one state batch).
+template <int D, bool kBf16>
+__global__ void __launch_bounds__(kThreads) merge_finalize_kernel(
+    const float *__restrict__ m, const float *__restrict__ l, const float4 *__restrict__ o,
+    void *__restrict__ o_out, float *__restrict__ lse, int64_t n_out_rows, int64_t hr,
+    int parts) {
+  constexpr int kLanesPerRow = D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / kLanesPerRow;
+  const int chunk = (int)(gid % kLanesPerRow);
+  if (row >= n_out_rows) return;
+  const int64_t b = row / hr, first = b * parts * hr + (row - b * hr);   // part 0's state row
+  float mx = -INFINITY;
+  for (int p = 0; p < parts; ++p) mx = fmaxf(mx, m[first + p * hr]);
+  float ls = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (mx != -INFINITY) {
+    for (int p = 0; p < parts; ++p) {
+      const int64_t sr = first + p * hr;
+      const float mp = m[sr];
+      if (mp == -INFINITY) continue;
+      const float w = expf(mp - mx);
+      const float4 x = o[sr * kLanesPerRow + chunk];
+      ls += w * l[sr];
+      acc = make_float4(acc.x + w * x.x, acc.y + w * x.y, acc.z + w * x.z, acc.w + w * x.w);
+    }
+  }
+  float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (ls > 0.f) r = make_float4(acc.x / ls, acc.y / ls, acc.z / ls, acc.w / ls);
+  const int64_t oi = row * kLanesPerRow + chunk;
+  if (o_out) {
+    if constexpr (kBf16) {
+      uint2 pk;
+      pk.x = pack_bf16x2(r.x, r.y);
+      pk.y = pack_bf16x2(r.z, r.w);
+      reinterpret_cast<uint2 *>(o_out)[oi] = pk;
+    } else {
+      reinterpret_cast<float4 *>(o_out)[oi] = r;
+    }
+  }
+  if (lse && chunk == 0) lse[row] = ls > 0.f ? mx + logf(ls) : -INFINITY;
+}
+
 unsigned grid_for(int64_t threads) {
   int64_t b = (threads + kThreads - 1) / kThreads;
   return (unsigned)(b < 1 ? 1 : b);
@@ -147,6 +195,25 @@ hipError_t launch_finalize(const float *m, const float *l, const float *o, void 
       finalize_kernel<64, true><<<grid, dim3(kThreads), 0, s>>>(m, l, o4, o_out, lse, n_rows);
     else
       finalize_kernel<64, false><<<grid, dim3(kThreads), 0, s>>>(m, l, o4, o_out, lse, n_rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_finalize(const float *m, const float *l, const float *o, void *o_out,
+                                 bool out_bf16, float *lse, int64_t n_out_rows, int64_t hr,
+                                 int parts, int d, hipStream_t s) {
+  const dim3 grid(grid_for(n_out_rows * (d / 4)));
+  const float4 *o4 = reinterpret_cast<const float4 *>(o);
+  if (d == 128) {
+    if (out_bf16)
+      merge_finalize_kernel<128, true><<<grid, dim3(kThreads), 0, s>>>(m, l, o4, o_out, lse, n_out_rows, hr, parts);
+    else
+      merge_finalize_kernel<128, false><<<grid, dim3(kThreads), 0, s>>>(m, l, o4, o_out, lse, n_out_rows, hr, parts);
+  } else {
+    if (out_bf16)
+      merge_finalize_kernel<64, true><<<grid, dim3(kThreads), 0, s>>>(m, l, o4, o_out, lse, n_out_rows, hr, parts);
+    else
+      merge_finalize_kernel<64, false><<<grid, dim3(kThreads), 0, s>>>(m, l, o4, o_out, lse, n_out_rows, hr, parts);
   }
   return hipGetLastError();
 }

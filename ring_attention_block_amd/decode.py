@@ -82,19 +82,18 @@ class ChunkedDecode:
     head_dim]: chunk c is a contiguous [heads, chunk_rows, head_dim] slab.  The
     query block [1, heads, rows, head_dim] is broadcast to every chunk and one
     ra_step launch folds all chunks at once (batch = chunks, so every chunk and
-    head has its own workgroups); the chunks' partial states are then reduced
-    by log2(chunks) ra_lse_merge launches, each merging the second half of the
-    remaining batch into the first (the merge is associative and commutative
-    up to rounding), and chunk 0 is finalized.  All on one stream, with no
-    cross-stream synchronisation.  chunks must be a power of two.
+    head has its own workgroups); one ra_merge_finalize launch then reduces
+    the chunks' partial states (the merge is associative and commutative up to
+    rounding) and writes the finalized output.  Two launches on one stream,
+    with no cross-stream synchronisation.
     """
 
     def __init__(self, q_shape, chunks: int, device="cuda", compute_stream=None):
         b, h, rows, d = q_shape
         if b != 1:
             raise ValueError("the query block must have batch 1")
-        if chunks < 1 or chunks & (chunks - 1):
-            raise ValueError(f"chunks={chunks} must be a power of two")
+        if chunks < 1:
+            raise ValueError(f"chunks={chunks} must be positive")
         self.chunks = chunks
         self.q_shape = tuple(q_shape)
         self.state = _lib.State(chunks, h, rows, d, device=device)
@@ -114,10 +113,5 @@ class ChunkedDecode:
             self.qb.copy_(q.expand(n, -1, -1, -1))
         _lib.step(self.state, self.qb, k, v, 0, 0, 1, False, scale, self.compute,
                   flags=_lib.RA_STEP_FRESH)
-        width = n
-        while width > 1:
-            width //= 2
-            _lib.lse_merge(self.state.batch_slice(0, width), self.state.batch_slice(width, width),
-                           self.compute)
-        return _lib.finalize(self.state.batch_slice(0, 1), out_dtype, self.compute, o_out=o_out,
-                             lse_out=lse_out)
+        return _lib.merge_finalize(self.state, n, out_dtype, self.compute, o_out=o_out,
+                                   lse_out=lse_out)

@@ -109,6 +109,7 @@ def test_skip_and_empty_enqueue_nothing(L):
     assert _step(L, _state(), kv_rows=0, causal=0, k=0, v=0) == _lib.RA_OK
     assert L.ra_state_init(ctypes.byref(empty), None) == _lib.RA_OK
     assert L.ra_finalize(ctypes.byref(empty), None, 0, None, None) == _lib.RA_OK
+    assert L.ra_merge_finalize(ctypes.byref(empty), 1, None, 0, None, None) == _lib.RA_OK
     assert L.ra_lse_merge(ctypes.byref(empty), ctypes.byref(_state(rows=0, m=0, l=0, o=0)), None) == 0
     assert L.ra_stage_block(None, None, 0, None) == _lib.RA_OK
 
@@ -121,6 +122,15 @@ def test_merge_finalize_stage_reject(L):
     assert L.ra_lse_merge(None, ctypes.byref(a), None) == _lib.RA_ERR_INVALID_ARG
     assert L.ra_finalize(ctypes.byref(a), FAKE, 5, None, None) == _lib.RA_ERR_INVALID_ARG
     assert L.ra_finalize(ctypes.byref(a), FAKE + 2, 0, None, None) == _lib.RA_ERR_INVALID_ARG
+    for parts in (0, -1, 3):
+        assert L.ra_merge_finalize(ctypes.byref(_state(batch=2)), parts, FAKE, 0, None,
+                                   None) == _lib.RA_ERR_INVALID_ARG
+    assert b"divide" in L.ra_last_error()
+    assert L.ra_merge_finalize(ctypes.byref(_state(batch=2)), 2, FAKE, 5, None,
+                               None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_merge_finalize(ctypes.byref(_state(batch=2)), 2, FAKE + 4, 0, None,
+                               None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_merge_finalize(None, 1, FAKE, 0, None, None) == _lib.RA_ERR_INVALID_ARG
     assert L.ra_stage_block(FAKE, None, 16, None) == _lib.RA_ERR_INVALID_ARG
     assert L.ra_stage_block(FAKE, FAKE + 8, 16, None) == _lib.RA_ERR_INVALID_ARG
     assert b"overlap" in L.ra_last_error()

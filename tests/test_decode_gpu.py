@@ -1,6 +1,8 @@
 """GPU parity of decoding: a short query block against P key/value shards
 (ShardedDecode: local ra_step per shard with kv_rows != rows, tree of
-ra_lse_merge, finalize) against the fp64 oracle over the whole cache.
+ra_lse_merge, finalize; ChunkedDecode: one ra_step over the shards as batch
+entries, one ra_merge_finalize) against the fp64 oracle over the whole cache,
+and ra_merge_finalize alone against the oracle's merge and finalize.
 
 Inputs come from ring_attention_block_amd.synth; expected values from oracle/.
 """
@@ -11,7 +13,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from oracle import dense
+from oracle import blockwise, dense
 from ring_attention_block_amd import _lib, synth
 from ring_attention_block_amd.decode import ShardedDecode
 
@@ -108,14 +110,16 @@ CHUNKED = [
     (2, 64, 5, 129, 4, "f32"),
     (1, 128, 300, 64, 1, "f32"),
     (2, 128, 7, 333, 16, "bf16"),
+    (2, 128, 3, 700, 3, "bf16"),
+    (1, 64, 33, 96, 5, "f32"),
 ]
 
 
 @pytest.mark.parametrize("heads,d,rq,c,n,dtype", CHUNKED)
 def test_chunked_decode(heads, d, rq, c, n, dtype):
     """ChunkedDecode (the cache as n chunks along the batch axis, one ra_step
-    launch over all chunks, halving merges, finalize) against the oracle over
-    the whole cache."""
+    launch over all chunks, one merge-and-finalize launch) against the oracle
+    over the whole cache."""
     from ring_attention_block_amd.decode import ChunkedDecode
     wl = synth.Workload(f"cdec_{dtype}_h{heads}_d{d}_q{rq}_c{c}_n{n}", 600 + rq + c, heads, d, c,
                         n + 1, dtype, False, (n,))
@@ -141,3 +145,72 @@ def test_chunked_decode(heads, d, rq, c, n, dtype):
         eo = assert_close(o[0, hh].cpu().numpy(), want_o[0], to, f"head {hh} O")
         el = assert_close(lse[0, hh].cpu().numpy(), want_lse[0], tl, f"head {hh} LSE")
     _say(f"  max|dO|={eo:.2e} max|dLSE|={el:.2e} (last head)")
+
+
+MERGE_CASES = [
+    # (output batch, parts, heads, rows, head_dim)
+    (2, 5, 3, 37, 64),
+    (1, 8, 2, 300, 128),
+    (3, 1, 1, 5, 128),
+    (1, 3, 4, 64, 64),
+]
+
+
+@pytest.mark.parametrize("out_batch,parts,heads,rows,d", MERGE_CASES)
+def test_merge_finalize_against_oracle(out_batch, parts, heads, rows, d):
+    """ra_merge_finalize over states that the oracle folded (some parts empty
+    for some rows, one row empty in every part) against the oracle's pairwise
+    merge and finalize of the same fp32-rounded states; and against
+    ra_lse_merge pairs plus ra_finalize on the GPU."""
+    wl = synth.Workload(f"mf_b{out_batch}_p{parts}_h{heads}_c{rows}_d{d}", 900 + rows + parts,
+                        heads, d, rows, parts + 1, "f32", False, (parts,))
+    _say(wl.name)
+    rng_rows = np.arange(rows)
+    st = _lib.State(out_batch * parts, heads, rows, d)
+    parts_f32 = {}
+    for b in range(out_batch):
+        for h in range(heads):
+            q = synth.block(wl, synth.ROLE_Q, parts, rows=rows)[h].astype(np.float64)
+            for p in range(parts):
+                k = synth.block(wl, synth.ROLE_K, p)[h].astype(np.float64) * (1 + b)
+                v = synth.block(wl, synth.ROLE_V, p)[h].astype(np.float64)
+                allowed = np.ones((rows, rows), dtype=bool)
+                allowed[(rng_rows + p + b) % 4 == 0] = False     # this part misses some rows
+                allowed[rows - 1] = False                        # a row no part sees
+                s_blk = (q @ k.T) * wl.scale
+                ost = blockwise.fold_block(blockwise.empty_state(rows, d), s_blk, v, allowed)
+                m32, l32, o32 = (x.astype(np.float32) for x in (ost.m, ost.l, ost.o))
+                parts_f32[(b, h, p)] = (m32, l32, o32)
+                sb = b * parts + p
+                st.m[sb, h] = torch.from_numpy(m32)
+                st.l[sb, h] = torch.from_numpy(l32)
+                st.o[sb, h] = torch.from_numpy(o32)
+    o, lse = _lib.merge_finalize(st, parts)
+    ob, _ = _lib.merge_finalize(st, parts, torch.bfloat16)
+    torch.cuda.synchronize()
+    for b in range(out_batch):
+        for h in range(heads):
+            acc = blockwise.empty_state(rows, d)
+            for p in range(parts):
+                m32, l32, o32 = parts_f32[(b, h, p)]
+                acc = blockwise.merge(acc, blockwise.State(m32.astype(np.float64),
+                                                           l32.astype(np.float64),
+                                                           o32.astype(np.float64)))
+            want_o, want_lse = blockwise.finalize(acc)
+            assert_close(o[b, h].cpu().numpy(), want_o, 1e-5, f"b{b} h{h} O")
+            assert_close(lse[b, h].cpu().numpy(), want_lse, 1e-5, f"b{b} h{h} LSE")
+            # bf16 output: round-to-nearest-even of the fp32 result (2^-9 relative)
+            assert_close(ob[b, h].float().cpu().numpy(), want_o,
+                         float(np.abs(want_o).max()) * 2 ** -8 + 1e-6, f"b{b} h{h} bf16 O")
+    assert bool((o[:, :, rows - 1] == 0).all()) and bool(torch.isneginf(lse[:, :, rows - 1]).all())
+    # Against the pairwise merges on the GPU (rounding order differs only).
+    want = []
+    for b in range(out_batch):
+        dst = st.batch_slice(b * parts, 1)
+        for p in range(1, parts):
+            _lib.lse_merge(dst, st.batch_slice(b * parts + p, 1))
+        want.append(_lib.finalize(dst))
+    torch.cuda.synchronize()
+    for b, (wo, wlse) in enumerate(want):
+        assert_close(o[b].cpu().numpy(), wo[0].cpu().numpy(), 1e-5, f"b{b} O vs pairwise")
+        assert_close(lse[b].cpu().numpy(), wlse[0].cpu().numpy(), 1e-5, f"b{b} LSE vs pairwise")
