@@ -118,19 +118,41 @@ __global__ void __launch_bounds__(kThreads) merge_finalize_kernel(
   const int chunk = (int)(gid % kLanesPerRow);
   if (row >= n_out_rows) return;
   const int64_t b = row / hr, first = b * parts * hr + (row - b * hr);   // part 0's state row
+  // Parts are taken kBatch at a time with every load of a batch issued
+  // before any use, so a thread waits for one memory round trip per batch
+  // rather than per part.
+  constexpr int kBatch = 8;
   float mx = -INFINITY;
-  for (int p = 0; p < parts; ++p) mx = fmaxf(mx, m[first + p * hr]);
+  for (int p0 = 0; p0 < parts; p0 += kBatch) {
+    float mv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      mv[u] = p0 + u < parts ? m[first + (int64_t)(p0 + u) * hr] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mx = fmaxf(mx, mv[u]);
+  }
   float ls = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (mx != -INFINITY) {
-    for (int p = 0; p < parts; ++p) {
-      const int64_t sr = first + p * hr;
-      const float mp = m[sr];
-      if (mp == -INFINITY) continue;
-      const float w = expf(mp - mx);
-      const float4 x = o[sr * kLanesPerRow + chunk];
-      ls += w * l[sr];
-      acc = make_float4(acc.x + w * x.x, acc.y + w * x.y, acc.z + w * x.z, acc.w + w * x.w);
+    for (int p0 = 0; p0 < parts; p0 += kBatch) {
+      float mv[kBatch], lv[kBatch];
+      float4 ov[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const bool in = p0 + u < parts;
+        const int64_t sr = first + (int64_t)(in ? p0 + u : 0) * hr;
+        mv[u] = in ? m[sr] : -INFINITY;
+        lv[u] = l[sr];
+        ov[u] = o[sr * kLanesPerRow + chunk];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (mv[u] == -INFINITY) continue;        // a part that saw no key adds nothing
+        const float w = expf(mv[u] - mx);
+        ls += w * lv[u];
+        acc = make_float4(acc.x + w * ov[u].x, acc.y + w * ov[u].y, acc.z + w * ov[u].z,
+                          acc.w + w * ov[u].w);
+      }
     }
   }
   float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
