@@ -71,6 +71,9 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                "ra_step_bf16_full_causal_h32_d128_c4096_hbm_traffic.md")
 BWD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
                                    "ra_bwd_step_bf16_full_causal_h32_d128_c4096_hbm_traffic.md")
+DEC_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                                   "ra_step_bf16_decode_h32_d128_shards8x4096_q16_hbm_traffic.md")
+DEC_TRAFFIC_ROWS = 16   # the query-block length the decode counters were taken at
 
 
 def timed_rings(args) -> int:
@@ -131,6 +134,43 @@ def cpu_baseline(wl, rank, blocks, target_s=15.0):
                       f"products, one thread for exp)"}
 
 
+def cpu_baseline_decode(wl, blocks, rq, target_s=15.0):
+    """The CPU fp64 oracle on the decode step, head by head (each head: the
+    rq query rows against all P x c keys, inputs converted to fp64 as the
+    oracle takes them) until about target_s / 3 seconds; the rate is the
+    key/value bytes of the heads done per second."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _helpers import oracle_values        # test plumbing around oracle/
+    from oracle import dense
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas")
+    except Exception:
+        blas_threads = None
+    P, c = wl.blocks, wl.rows
+    qh = synth.block(wl, synth.ROLE_Q, P, rows=rq)
+    kp, qp = np.arange(P * c), np.full(rq, P * c)
+    esize = 2 if wl.dtype == "bf16" else 4
+    done, t0 = 0, time.perf_counter()
+    while done < wl.heads:
+        h = done
+        k = np.concatenate([oracle_values(blocks[(synth.ROLE_K, j)][h:h + 1], wl) for j in range(P)],
+                           axis=1)
+        v = np.concatenate([oracle_values(blocks[(synth.ROLE_V, j)][h:h + 1], wl) for j in range(P)],
+                           axis=1)
+        dense.attention(oracle_values(qh[h:h + 1], wl), k, v, qp, kp, False, wl.scale)
+        done += 1
+        if time.perf_counter() - t0 >= target_s / 3:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = 2 * P * c * wl.head_dim * esize * done
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"{rq} query rows x {done} of {wl.heads} heads against {P} x {c} keys "
+                      f"({nbytes / 1e6:.0f} MB of keys and values, {dt:.1f} s; numpy BLAS threads "
+                      f"for the products, one thread for exp)"}
+
+
 def bench_decode(args, wl):
     """Decode: args.decode_rows query rows (the tokens after the sequence)
     against the workload's P blocks as key/value shards, laid out as chunks
@@ -160,11 +200,19 @@ def bench_decode(args, wl):
     for _ in range(args.warmup):
         dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
     torch.cuda.synchronize()
+    # The step kernel of one timed step in time_every carries timing events
+    # bound to its dispatch.
+    n_timed = len(range(0, args.steps, args.time_every))
+    pool = iter([Event(timing=True) for _ in range(2 * n_timed)])
+    timers = []
     e0, e1 = Event(timing=True), Event(timing=True)
     t0 = time.perf_counter()
     e0.record(compute)
-    for _ in range(args.steps):
-        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
+    for s in range(args.steps):
+        ev = (next(pool), next(pool)) if s % args.time_every == 0 else (None, None)
+        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse, start=ev[0], stop=ev[1])
+        if ev[0] is not None:
+            timers.append(ev)
     e1.record(compute)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -172,6 +220,13 @@ def bench_decode(args, wl):
     esize = 2 if wl.dtype == "bf16" else 4
     kv_bytes = 2 * P * c * wl.heads * wl.head_dim * esize
     flops = 4 * wl.head_dim * wl.heads * rq * P * c
+    # Algorithmic bytes of the fold launch: the broadcast query block and the
+    # cache read, the P partial states written (m, l, O in fp32; the fresh
+    # fold reads no state).
+    step_bytes = kv_bytes + P * wl.heads * rq * (wl.head_dim * esize + (wl.head_dim + 2) * 4)
+    step_ms = float(np.mean([a.elapsed_time(b) for a, b in timers]))
+    achieved = step_bytes / (step_ms / 1e3) / 1e9
+    peak = PEAK_HBM_BYTES / 1e9
     line = {
         "metric": "decode key/value read rate (GB/s)", "value": round(kv_bytes / (ms / 1e3) / 1e9, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -184,8 +239,17 @@ def bench_decode(args, wl):
                    "kv_bytes": kv_bytes, "flop_per_step": flops,
                    "tflops": round(flops / (ms / 1e3) / 1e12, 2),
                    "pct_of_hbm_peak": round(100 * kv_bytes / (ms / 1e3) / PEAK_HBM_BYTES, 2)},
+        "roofline": {"bound": "hbm", "kernel": "ra_step decode fold", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "GB/s", "frac": round(achieved / peak, 4),
+                     "traffic": (measured_traffic(wl, DEC_TRAFFIC_PROFILE)
+                                 if rq == DEC_TRAFFIC_ROWS else None),
+                     "bytes_per_launch": step_bytes,
+                     "avg_launch_ms": round(step_ms, 5), "launches": len(timers),
+                     "timed_steps": f"1 in {args.time_every} of the {args.steps} timed steps"},
         "compute_stream_ms": round(e0.elapsed_time(e1) / args.steps, 4),
     }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(wl, blocks, rq)
     print(json.dumps(line), flush=True)
 
 

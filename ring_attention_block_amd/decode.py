@@ -101,9 +101,10 @@ class ChunkedDecode:
         self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
-            out_dtype=torch.float32, o_out=None, lse_out=None):
+            out_dtype=torch.float32, o_out=None, lse_out=None, start=None, stop=None):
         """k, v: [chunks, heads, chunk_rows, head_dim].  Returns the finalized
-        (O, LSE) of q against all chunks."""
+        (O, LSE) of q against all chunks.  start, stop: optional timing events
+        bound to the fold's step kernel (ra_step_timed)."""
         n = self.chunks
         if tuple(k.shape[:2]) != (n, self.q_shape[1]) or k.shape != v.shape:
             raise ValueError(f"k, v must be [{n}, {self.q_shape[1]}, chunk_rows, d]")
@@ -112,6 +113,6 @@ class ChunkedDecode:
         with torch.cuda.stream(self.compute):
             self.qb.copy_(q.expand(n, -1, -1, -1))
         _lib.step(self.state, self.qb, k, v, 0, 0, 1, False, scale, self.compute,
-                  flags=_lib.RA_STEP_FRESH)
+                  flags=_lib.RA_STEP_FRESH, start=start, stop=stop)
         return _lib.merge_finalize(self.state, n, out_dtype, self.compute, o_out=o_out,
                                    lse_out=lse_out)
