@@ -253,6 +253,48 @@ def bench_decode(args, wl):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_backward(wl, rank, blocks, target_s=15.0):
+    """The CPU fp64 oracle's dense attention backward (dQ, dK, dV), as it
+    stands, on a bounded sample of rank's query rows against the key blocks
+    its backward ring visits, every head; FLOPs as for the GPU line (10 x
+    head_dim per unmasked pair per head)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _helpers import oracle_values        # test plumbing around oracle/
+    from oracle import backward, dense
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas")
+    except Exception:
+        blas_threads = None
+    kv_blocks = list(range(rank + 1)) if wl.causal else list(range(wl.blocks))
+    kp = np.concatenate([dense.ring_positions(j, wl.rows) for j in kv_blocks])
+    n = 4
+    while True:
+        rows = synth.sample_rows(wl.seed, wl.rows, n)
+        qp = dense.ring_positions(rank, wl.rows)[rows]
+        t0 = time.perf_counter()
+        for h in range(wl.heads):
+            kh = np.concatenate([oracle_values(blocks[(synth.ROLE_K, j)][h:h + 1], wl)
+                                 for j in kv_blocks], axis=1)
+            vh = np.concatenate([oracle_values(blocks[(synth.ROLE_V, j)][h:h + 1], wl)
+                                 for j in kv_blocks], axis=1)
+            backward.attention_backward(oracle_values(blocks[(synth.ROLE_Q, rank)][h:h + 1, rows], wl),
+                                        kh, vh,
+                                        oracle_values(blocks[(synth.ROLE_DO, rank)][h:h + 1, rows], wl),
+                                        qp, kp, wl.causal, wl.scale)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or n >= wl.rows:
+            break
+        n = min(wl.rows, int(n * max(2.0, target_s / 3 / max(dt, 1e-3))))
+    flops = 10 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank, rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} seeded query rows x {wl.heads} heads of rank {rank}, backward "
+                      f"({flops / 1e9:.1f} GFLOP fp64, {dt:.1f} s; numpy BLAS threads for the "
+                      f"products, one thread for exp)"}
+
+
 def bench_backward(args, wl, rank):
     """Backward ring of `rank`: D = rowsum(dO * O) (ra_bwd_prepare), then the P
     ring steps with dK, dV travelling with the visiting block (staged in,
@@ -371,6 +413,8 @@ def bench_backward(args, wl, rank):
                      "timed_rings": f"1 in {args.time_every} of the {args.steps} timed rings",
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
     }
+    if not args.no_cpu_baseline and not zigzag:
+        line["cpu_baseline"] = cpu_baseline_backward(wl, rank, blocks)
     print(json.dumps(line), flush=True)
 
 
