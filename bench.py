@@ -220,9 +220,9 @@ def bench_decode(args, wl):
     esize = 2 if wl.dtype == "bf16" else 4
     kv_bytes = 2 * P * c * wl.heads * wl.head_dim * esize
     flops = 4 * wl.head_dim * wl.heads * rq * P * c
-    # Algorithmic bytes of the fold launch: the broadcast query block and the
-    # cache read, the P partial states written (m, l, O in fp32; the fresh
-    # fold reads no state).
+    # Algorithmic bytes of the fold launch: the cache and the query block as
+    # the P chunks' workgroups read it, the P partial states written (m, l, O
+    # in fp32; the fresh fold reads no state).
     step_bytes = kv_bytes + P * wl.heads * rq * (wl.head_dim * esize + (wl.head_dim + 2) * 4)
     step_ms = float(np.mean([a.elapsed_time(b) for a, b in timers]))
     achieved = step_bytes / (step_ms / 1e3) / 1e9

@@ -64,8 +64,10 @@ typedef enum { RA_CASE_SKIP = 0, RA_CASE_DIAG = 1, RA_CASE_FULL = 2 } ra_case;
 typedef enum {
   RA_STEP_FRESH = 1,    /* the state is not read: the step starts from the empty
                            state, as right after ra_state_init */
-  RA_STEP_FINALIZE = 2  /* the step writes ra_finalize's outputs instead of the
+  RA_STEP_FINALIZE = 2, /* the step writes ra_finalize's outputs instead of the
                            state, which keeps its previous contents */
+  RA_STEP_Q_BROADCAST = 4 /* q holds one batch entry, [1, heads, rows, head_dim],
+                             read by every batch entry of the state and of k, v */
 } ra_step_flags;
 
 /*
@@ -143,12 +145,18 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
  * "Accumulation math, step by step": out = O / l; the saved LSE of the
  * backward section of "Ring Attention：把超长序列沿设备环流动"), so a ring needs
  * no separate init and finalize launches.  Arguments as in ra_step, plus:
- *   flags      0, RA_STEP_FRESH, RA_STEP_FINALIZE or both (else
- *              RA_ERR_INVALID_ARG).  RA_STEP_FRESH: m, l and o are not read;
+ *   flags      any combination of RA_STEP_FRESH, RA_STEP_FINALIZE and
+ *              RA_STEP_Q_BROADCAST (else RA_ERR_INVALID_ARG).  RA_STEP_FRESH:
+ *              m, l and o are not read;
  *              the result is that of ra_state_init followed by ra_step.
  *              RA_STEP_FINALIZE: instead of storing the new state the step
  *              writes o_out and lse_out exactly as ra_finalize would from it
  *              (bit-identical); m, l and o keep their previous contents.
+ *              RA_STEP_Q_BROADCAST: q is [1, heads, rows, head_dim] and batch
+ *              entry b of the state folds it against batch entry b of k, v
+ *              (decoding one query block against a cache laid out as chunks
+ *              along the batch axis, without copying the query block per
+ *              chunk); the result is that of a q repeated along the batch.
  *   o_out, out_dtype, lse_out   as in ra_finalize (used with
  *              RA_STEP_FINALIZE only; either may be NULL; 16-byte aligned).
  * A step that folds nothing (a skipped causal block, kv_rows == 0) still

@@ -157,7 +157,7 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
-RA_STEP_FRESH, RA_STEP_FINALIZE = 1, 2
+RA_STEP_FRESH, RA_STEP_FINALIZE, RA_STEP_Q_BROADCAST = 1, 2, 4
 
 
 def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
@@ -176,10 +176,11 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
             raise ValueError(f"{name} must be contiguous")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
+    q_batch = 1 if flags & RA_STEP_Q_BROADCAST else k.shape[0]
     if k.shape != v.shape or k.dim() != 4 or q.dim() != 4 or \
-            (q.shape[0], q.shape[1], q.shape[3]) != (k.shape[0], k.shape[1], k.shape[3]):
+            (q.shape[0], q.shape[1], q.shape[3]) != (q_batch, k.shape[1], k.shape[3]):
         raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
-    if tuple(q.shape) != st.shape:
+    if (k.shape[0], *q.shape[1:]) != st.shape:
         raise ValueError(f"q shape {tuple(q.shape)} does not match the state {st.shape}")
     if flags == 0 and start is None and stop is None:
         _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),

@@ -144,7 +144,7 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
     return fail(RA_ERR_UNSUPPORTED, "%s: bf16 blocks must stay below 2^31 bytes per (batch, head)", name);
   if (!(scale > 0.f) || !isfinite(scale))
     return fail(RA_ERR_INVALID_ARG, "%s: scale=%g must be finite and > 0", name, (double)scale);
-  if (flags & ~(uint32_t)(RA_STEP_FRESH | RA_STEP_FINALIZE))
+  if (flags & ~(uint32_t)(RA_STEP_FRESH | RA_STEP_FINALIZE | RA_STEP_Q_BROADCAST))
     return fail(RA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, (unsigned)flags);
   if (flags & RA_STEP_FINALIZE) {
     if (out_dtype != RA_F32 && out_dtype != RA_BF16)
@@ -195,6 +195,7 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   a.rows = st->rows;
   a.kv_rows = kv_rows;
   a.bh = st->batch * st->heads;
+  a.q_bh = (flags & RA_STEP_Q_BROADCAST) ? st->heads : a.bh;
   a.scale_log2 = scale * 1.442695040888963407f;
   a.flags = (flags & RA_STEP_FRESH ? ra::kStepFresh : 0u) | (flags & RA_STEP_FINALIZE ? ra::kStepFinalize : 0u);
   a.o_out = (flags & RA_STEP_FINALIZE) ? o_out : nullptr;

@@ -16,6 +16,7 @@ struct StepArgs {
   int32_t rows;           // query rows of the block
   int32_t kv_rows;        // key/value rows of the visiting block (== rows for a diagonal block)
   int32_t bh;             // batch * heads
+  int32_t q_bh;           // (batch, head) entries of q: q entry of bh is bh % q_bh
   float scale_log2;       // score scale * log2(e): kernels work in base 2
   uint32_t flags;         // kStepFresh, kStepFinalize
   void *o_out;            // kStepFinalize: O / l ([bh, rows, D], fp32 or bf16), may be NULL

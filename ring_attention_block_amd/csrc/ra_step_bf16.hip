@@ -303,7 +303,8 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
 
   const size_t base = (size_t)bh * rows * D;
   const size_t kv_base = (size_t)bh * kv_rows * D;
-  const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.q) + base;
+  const int q_bh = bh < a.q_bh ? bh : bh % a.q_bh;   // a query block shared along the batch
+  const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.q) + (size_t)q_bh * rows * D;
   float *__restrict__ O = a.o + base;
   // The query rows and the state are read through buffer resources whose
   // range check returns 0 past the block end and, for the state, for every row

@@ -37,7 +37,8 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
   const bool row_ok = row < rows;
   const size_t base = (size_t)bh * rows * D;
   const size_t kv_base = (size_t)bh * kv_rows * D;
-  const float *__restrict__ Q = static_cast<const float *>(a.q) + base;
+  const int q_bh = bh < a.q_bh ? bh : bh % a.q_bh;   // a query block shared along the batch
+  const float *__restrict__ Q = static_cast<const float *>(a.q) + (size_t)q_bh * rows * D;
   const float *__restrict__ K = static_cast<const float *>(a.k) + kv_base;
   const float *__restrict__ V = static_cast<const float *>(a.v) + kv_base;
   float *__restrict__ O = a.o + base;

@@ -79,10 +79,11 @@ class ChunkedDecode:
     """Decode with the key/value cache laid out as chunks along the batch axis.
 
     The cache (all shards) is held as K, V of shape [chunks, heads, chunk_rows,
-    head_dim]: chunk c is a contiguous [heads, chunk_rows, head_dim] slab.  The
-    query block [1, heads, rows, head_dim] is broadcast to every chunk and one
-    ra_step launch folds all chunks at once (batch = chunks, so every chunk and
-    head has its own workgroups); one ra_merge_finalize launch then reduces
+    head_dim]: chunk c is a contiguous [heads, chunk_rows, head_dim] slab.  One
+    ra_step launch folds the query block [1, heads, rows, head_dim] against all
+    chunks at once (RA_STEP_Q_BROADCAST: every batch entry of the state reads
+    the one query block; batch = chunks, so every chunk and head has its own
+    workgroups); one ra_merge_finalize launch then reduces
     the chunks' partial states (the merge is associative and commutative up to
     rounding) and writes the finalized output.  Two launches on one stream,
     with no cross-stream synchronisation.
@@ -97,7 +98,6 @@ class ChunkedDecode:
         self.chunks = chunks
         self.q_shape = tuple(q_shape)
         self.state = _lib.State(chunks, h, rows, d, device=device)
-        self.qb = torch.empty((chunks, h, rows, d), dtype=torch.bfloat16, device=device)
         self.compute = compute_stream if compute_stream is not None else torch.cuda.current_stream()
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
@@ -108,11 +108,9 @@ class ChunkedDecode:
         n = self.chunks
         if tuple(k.shape[:2]) != (n, self.q_shape[1]) or k.shape != v.shape:
             raise ValueError(f"k, v must be [{n}, {self.q_shape[1]}, chunk_rows, d]")
-        if self.qb.dtype != q.dtype:
-            self.qb = torch.empty(self.qb.shape, dtype=q.dtype, device=self.qb.device)
-        with torch.cuda.stream(self.compute):
-            self.qb.copy_(q.expand(n, -1, -1, -1))
-        _lib.step(self.state, self.qb, k, v, 0, 0, 1, False, scale, self.compute,
-                  flags=_lib.RA_STEP_FRESH, start=start, stop=stop)
+        if tuple(q.shape) != self.q_shape:
+            raise ValueError(f"q must be {self.q_shape}")
+        _lib.step(self.state, q, k, v, 0, 0, 1, False, scale, self.compute,
+                  flags=_lib.RA_STEP_FRESH | _lib.RA_STEP_Q_BROADCAST, start=start, stop=stop)
         return _lib.merge_finalize(self.state, n, out_dtype, self.compute, o_out=o_out,
                                    lse_out=lse_out)

@@ -184,8 +184,11 @@ def test_step_ex_rejects_before_enqueue(L):
         args.update(kw)
         return L.ra_step_ex(ctypes.byref(st), args["q"], args["k"], args["v"], _lib.RA_BF16, st.rows,
                             args["i"], args["j"], args["P"], args["causal"], 0.125, flags, o, ot, lse, None)
-    assert ex(4) == _lib.RA_ERR_INVALID_ARG
+    assert ex(8) == _lib.RA_ERR_INVALID_ARG
     assert b"ra_step_ex" in L.ra_last_error() and b"flags" in L.ra_last_error()
+    # the query broadcast flag is accepted (a skipped block enqueues nothing)
+    assert ex(_lib.RA_STEP_Q_BROADCAST, i=0, j=1) == _lib.RA_OK
+    assert ex(_lib.RA_STEP_Q_BROADCAST | _lib.RA_STEP_FRESH, q=0) == _lib.RA_ERR_INVALID_ARG
     assert ex(_lib.RA_STEP_FINALIZE, ot=3) == _lib.RA_ERR_INVALID_ARG
     assert ex(_lib.RA_STEP_FINALIZE, o=FAKE + 8) == _lib.RA_ERR_INVALID_ARG
     assert ex(_lib.RA_STEP_FINALIZE, lse=FAKE + 4) == _lib.RA_ERR_INVALID_ARG
@@ -206,7 +209,7 @@ def test_timed_entries_reject_before_enqueue(L):
         return L.ra_step_timed(ctypes.byref(st), args["q"], args["k"], args["v"], _lib.RA_BF16,
                                st.rows, args["i"], args["j"], args["P"], args["causal"],
                                args["scale"], flags, FAKE, _lib.RA_F32, FAKE, bogus, bogus, None)
-    assert timed(flags=4) == _lib.RA_ERR_INVALID_ARG
+    assert timed(flags=8) == _lib.RA_ERR_INVALID_ARG
     assert b"ra_step_timed" in L.ra_last_error() and b"flags" in L.ra_last_error()
     assert timed(i=2) == _lib.RA_ERR_INVALID_ARG
     assert timed(q=0) == _lib.RA_ERR_INVALID_ARG

@@ -214,3 +214,32 @@ def test_merge_finalize_against_oracle(out_batch, parts, heads, rows, d):
     for b, (wo, wlse) in enumerate(want):
         assert_close(o[b].cpu().numpy(), wo[0].cpu().numpy(), 1e-5, f"b{b} O vs pairwise")
         assert_close(lse[b].cpu().numpy(), wlse[0].cpu().numpy(), 1e-5, f"b{b} LSE vs pairwise")
+
+
+@pytest.mark.parametrize("dtype,d,rows,kv_rows,chunks,heads",
+                         [("bf16", 128, 16, 4096, 8, 32), ("bf16", 64, 300, 129, 3, 2),
+                          ("bf16", 128, 1000, 512, 2, 4), ("f32", 64, 5, 200, 4, 2)])
+def test_query_broadcast_is_bit_identical(dtype, d, rows, kv_rows, chunks, heads):
+    """ra_step with RA_STEP_Q_BROADCAST (one query block for every batch entry)
+    gives exactly what the same step gives with the query block repeated along
+    the batch, with and without the fresh and finalize flags."""
+    wl = synth.Workload(f"qbc_{dtype}_d{d}_q{rows}_c{kv_rows}_n{chunks}", 950 + rows, heads, d, kv_rows,
+                        chunks + 1, dtype, False, (chunks,))
+    _say(wl.name)
+    q1 = to_device(synth.block(wl, synth.ROLE_Q, chunks, rows=rows), wl)
+    k = torch.cat([to_device(synth.block(wl, synth.ROLE_K, j), wl) for j in range(chunks)]).contiguous()
+    v = torch.cat([to_device(synth.block(wl, synth.ROLE_V, j), wl) for j in range(chunks)]).contiguous()
+    qn = q1.expand(chunks, -1, -1, -1).contiguous()
+    for flags in (0, _lib.RA_STEP_FRESH, _lib.RA_STEP_FRESH | _lib.RA_STEP_FINALIZE):
+        res = []
+        for q, extra in ((qn, 0), (q1, _lib.RA_STEP_Q_BROADCAST)):
+            st = _lib.State(chunks, heads, rows, d)
+            _lib.state_init(st)
+            o = torch.full(st.o.shape, float("nan"), device="cuda")
+            lse = torch.full(st.m.shape, float("nan"), device="cuda")
+            _lib.step(st, q, k, v, 0, 0, 1, False, wl.scale, flags=flags | extra, o_out=o,
+                      lse_out=lse)
+            torch.cuda.synchronize()
+            res.append([t.clone() for t in (st.m, st.l, st.o, o, lse)])
+        for a, b in zip(*res):
+            assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0)), f"flags={flags}"
