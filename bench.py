@@ -351,11 +351,8 @@ def bench_backward(args, wl, rank):
     del states
 
     def one_ring(timers=None, pool=None):
-        with torch.cuda.stream(compute):
-            for dq in dqs:
-                dq.zero_()
-        for (o, _), do, delta in zip(outs, dos, deltas):
-            _lib.bwd_prepare(o, do, delta, stream=compute)
+        for (o, _), do, delta, dq in zip(outs, dos, deltas, dqs):
+            _lib.bwd_prepare(o, do, delta, stream=compute, dq=dq)   # also zeroes dQ
         lses = [lse for _, lse in outs]
         if zigzag:
             ring.run_backward(qs, dos, lses, deltas, dqs, source, rank, wl.blocks, wl.causal,

@@ -258,12 +258,15 @@ ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t s
  *   dout    [batch, heads, rows, head_dim] gradient of the loss with respect
  *           to that output, in do_dtype
  *   delta   [batch, heads, rows] fp32, written
+ *   dq      [batch, heads, rows, head_dim] fp32, set to zero (the rank's dQ
+ *           accumulator before its backward ring); may be NULL to skip;
+ *           16-byte aligned
  * head_dim 64 or 128 (else RA_ERR_UNSUPPORTED); checks and errors as for
  * ra_step.
  */
 ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
                          const void *o, ra_dtype o_dtype, const void *dout, ra_dtype do_dtype,
-                         float *delta, hipStream_t stream);
+                         float *delta, float *dq, hipStream_t stream);
 
 /*
  * Backward of one ring step: the contribution of visiting block j to the

@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
             "ra_merge_finalize": (ctypes.c_int, [sp, i32, vp, ctypes.c_int, vp, vp]),
             "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
             "ra_bwd_prepare": (ctypes.c_int, [i32, i32, i32, i32, vp, ctypes.c_int, vp, ctypes.c_int,
-                                              vp, vp]),
+                                              vp, vp, vp]),
             "ra_bwd_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_int,
                                            vp, vp, vp, i32, i32, i32, i32, f32, vp]),
             "ra_bwd_step_timed": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
@@ -252,8 +252,9 @@ def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
                                 _stream(stream)))
 
 
-def bwd_prepare(o, dout, delta=None, stream=None):
-    """delta = rowsum(dout * o) [B,H,rows] fp32 (o: the forward output)."""
+def bwd_prepare(o, dout, delta=None, stream=None, dq=None):
+    """delta = rowsum(dout * o) [B,H,rows] fp32 (o: the forward output); dq, if
+    given (fp32, o's shape), is set to zero in the same launch."""
     for name, t in (("o", o), ("dout", dout)):
         if not t.is_contiguous() or t.dim() != 4:
             raise ValueError(f"{name} must be a contiguous [B,H,rows,d] tensor")
@@ -262,8 +263,11 @@ def bwd_prepare(o, dout, delta=None, stream=None):
     b, h, r, d = o.shape
     if delta is None:
         delta = torch.empty((b, h, r), dtype=torch.float32, device=o.device)
+    if dq is not None and (tuple(dq.shape) != (b, h, r, d) or dq.dtype != torch.float32
+                           or not dq.is_contiguous()):
+        raise ValueError("dq must be a contiguous fp32 tensor of o's shape")
     _check(lib().ra_bwd_prepare(b, h, r, d, _ptr(o), _dtype_code(o), _ptr(dout), _dtype_code(dout),
-                                _ptr(delta), _stream(stream)))
+                                _ptr(delta), _ptr(dq), _stream(stream)))
     return delta
 
 

@@ -38,6 +38,7 @@ template <int D, typename OT, typename DT>
 __global__ void __launch_bounds__(256) bwd_prepare_kernel(const OT *__restrict__ o,
                                                           const DT *__restrict__ dout,
                                                           float *__restrict__ delta,
+                                                          float *__restrict__ dq,
                                                           int64_t n_rows) {
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int l = threadIdx.x & 15;
@@ -52,6 +53,10 @@ __global__ void __launch_bounds__(256) bwd_prepare_kernel(const OT *__restrict__
   acc += __shfl_xor(acc, 4);
   acc += __shfl_xor(acc, 8);
   if (row < n_rows && l == 0) delta[row] = acc;
+  if (dq && row < n_rows) {     // the rank's dQ accumulator starts at zero
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) dq[(size_t)row * D + 16 * i + l] = 0.f;
+  }
 }
 
 constexpr int kRows = 64;     // query rows per workgroup
@@ -164,25 +169,25 @@ hipError_t launch_simple_d(const BwdArgs &a, bool diag, hipStream_t s, const Lau
 
 template <int D>
 hipError_t launch_prepare_d(const void *o, bool o_bf16, const void *dout, bool do_bf16,
-                            float *delta, int64_t n_rows, hipStream_t s) {
+                            float *delta, float *dq, int64_t n_rows, hipStream_t s) {
   const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
   const float *of = static_cast<const float *>(o);
   const uint16_t *ob = static_cast<const uint16_t *>(o);
   const float *df = static_cast<const float *>(dout);
   const uint16_t *db = static_cast<const uint16_t *>(dout);
-  if (o_bf16 && do_bf16) bwd_prepare_kernel<D><<<grid, block, 0, s>>>(ob, db, delta, n_rows);
-  else if (o_bf16) bwd_prepare_kernel<D><<<grid, block, 0, s>>>(ob, df, delta, n_rows);
-  else if (do_bf16) bwd_prepare_kernel<D><<<grid, block, 0, s>>>(of, db, delta, n_rows);
-  else bwd_prepare_kernel<D><<<grid, block, 0, s>>>(of, df, delta, n_rows);
+  if (o_bf16 && do_bf16) bwd_prepare_kernel<D><<<grid, block, 0, s>>>(ob, db, delta, dq, n_rows);
+  else if (o_bf16) bwd_prepare_kernel<D><<<grid, block, 0, s>>>(ob, df, delta, dq, n_rows);
+  else if (do_bf16) bwd_prepare_kernel<D><<<grid, block, 0, s>>>(of, db, delta, dq, n_rows);
+  else bwd_prepare_kernel<D><<<grid, block, 0, s>>>(of, df, delta, dq, n_rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_prepare(const void *o, bool o_bf16, const void *dout, bool do_bf16,
-                              float *delta, int64_t n_rows, int d, hipStream_t s) {
-  if (d == 128) return launch_prepare_d<128>(o, o_bf16, dout, do_bf16, delta, n_rows, s);
-  return launch_prepare_d<64>(o, o_bf16, dout, do_bf16, delta, n_rows, s);
+                              float *delta, float *dq, int64_t n_rows, int d, hipStream_t s) {
+  if (d == 128) return launch_prepare_d<128>(o, o_bf16, dout, do_bf16, delta, dq, n_rows, s);
+  return launch_prepare_d<64>(o, o_bf16, dout, do_bf16, delta, dq, n_rows, s);
 }
 
 hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s,

@@ -293,7 +293,7 @@ ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_d
 
 ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t head_dim,
                          const void *o, ra_dtype o_dtype, const void *dout, ra_dtype do_dtype,
-                         float *delta, hipStream_t stream) {
+                         float *delta, float *dq, hipStream_t stream) {
   int64_t n = 0;
   ra_status s = check_shape(batch, heads, rows, head_dim, "ra_bwd_prepare", &n);
   if (s != RA_OK) return s;
@@ -304,8 +304,10 @@ ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t hea
     return fail(RA_ERR_INVALID_ARG,
                 "ra_bwd_prepare: o, dout and delta must be non-NULL and 16-byte aligned");
   (void)hipGetLastError();
+  if (dq && !aligned16(dq))
+    return fail(RA_ERR_INVALID_ARG, "ra_bwd_prepare: dq must be 16-byte aligned");
   return hip_status(ra::launch_bwd_prepare(o, o_dtype == RA_BF16, dout, do_dtype == RA_BF16, delta,
-                                           n, head_dim, stream),
+                                           dq, n, head_dim, stream),
                     "ra_bwd_prepare launch");
 }
 

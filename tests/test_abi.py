@@ -167,13 +167,14 @@ def test_bwd_rejects_before_enqueue(L):
     prep = lambda **kw: L.ra_bwd_prepare(1, 2, kw.get("rows", 128), kw.get("d", 128),
                                          kw.get("o", FAKE), kw.get("ot", _lib.RA_F32),
                                          kw.get("dout", FAKE), kw.get("dt", _lib.RA_BF16),
-                                         kw.get("delta", FAKE), None)
+                                         kw.get("delta", FAKE), kw.get("dq", None), None)
     assert prep(d=32) == _lib.RA_ERR_UNSUPPORTED
     assert prep(ot=4) == _lib.RA_ERR_INVALID_ARG
     assert prep(dt=4) == _lib.RA_ERR_INVALID_ARG
     for name in ("o", "dout", "delta"):
         assert prep(**{name: 0}) == _lib.RA_ERR_INVALID_ARG, name
         assert prep(**{name: FAKE + 8}) == _lib.RA_ERR_INVALID_ARG, name
+    assert prep(dq=FAKE + 4) == _lib.RA_ERR_INVALID_ARG
     assert prep(rows=0, o=0, dout=0, delta=0) == _lib.RA_OK
 
 

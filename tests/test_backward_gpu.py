@@ -215,8 +215,10 @@ def test_bwd_prepare_row_dot(heads, d, rows, o_dtype, do_dtype):
     wl_d = synth.Workload("prep_do", 72 + rows, heads, d, rows, 1, do_dtype, False, (0,))
     o_h = synth.block(wl_o, synth.ROLE_Q, 0)
     d_h = synth.block(wl_d, synth.ROLE_DO, 0)
-    got = _lib.bwd_prepare(to_device(o_h, wl_o), to_device(d_h, wl_d))
+    dq = torch.full((1, heads, rows, d), float("nan"), device="cuda")
+    got = _lib.bwd_prepare(to_device(o_h, wl_o), to_device(d_h, wl_d), dq=dq)
     torch.cuda.synchronize()
+    assert bool((dq == 0).all())                 # the dQ accumulator is cleared in the same launch
     want = backward.row_dot(oracle_values(d_h, wl_d), oracle_values(o_h, wl_o))
     bound = np.sum(np.abs(oracle_values(d_h, wl_d) * oracle_values(o_h, wl_o)), axis=-1)
     err = np.abs(got[0].cpu().numpy().astype(np.float64) - want)
