@@ -174,8 +174,8 @@ def cpu_baseline_decode(wl, blocks, rq, target_s=15.0):
 def bench_decode(args, wl):
     """Decode: args.decode_rows query rows (the tokens after the sequence)
     against the workload's P blocks as key/value shards, laid out as chunks
-    along the batch axis (ChunkedDecode: one ra_step launch over all shards,
-    log2(P) halving merges, finalize).  Memory-bound: the figure of merit is
+    along the batch axis (ChunkedDecode: one ra_step launch over all shards
+    reading the one query block, one ra_merge_finalize).  Memory-bound: the figure of merit is
     the key/value bytes read per second."""
     import torch
     from ring_attention_block_amd.decode import ChunkedDecode
@@ -434,7 +434,7 @@ def main():
     ap.add_argument("--decode-rows", type=int, default=None,
                     help="instead of the ring: decode this many query rows against the "
                          "workload's P blocks as key/value shards (all shards folded by one "
-                         "launch along the batch axis, halving merges, finalize)")
+                         "launch along the batch axis, one merge-and-finalize launch)")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward ring: the rank's backward ring (D, then the "
                          "P gradient steps with dK, dV travelling with the blocks)")

@@ -13,9 +13,11 @@ up to rounding.
 The shards hold keys that every new token may see (the history before the
 block; a single new token's own key may be the last one), so the local folds
 run without the causal mask; that is what lets ra_step take a key/value block
-of another length than the query block.  Here the ranks are P streams of one GPU: the local folds run
-concurrently, and a binary tree of ra_lse_merge calls reduces the P states into
-state 0 on the compute stream, which then finalizes.
+of another length than the query block.  ShardedDecode runs the P ranks as P
+streams of one GPU: the local folds run concurrently, and a binary tree of
+ra_lse_merge calls reduces the P states into state 0 on the compute stream,
+which then finalizes.  ChunkedDecode folds every shard in one launch and
+reduces and finalizes in a second one (ra_merge_finalize).
 """
 from __future__ import annotations
 
