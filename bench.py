@@ -76,6 +76,116 @@ DEC_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
 DEC_TRAFFIC_ROWS = 16   # the query-block length the decode counters were taken at
 
 
+def software_versions() -> dict:
+    """ROCm, HIP runtime, torch and device identity of the run."""
+    import torch
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"rocm": rocm, "hip": torch.version.hip, "torch": torch.__version__,
+            "numpy": np.__version__, "device": props.name,
+            "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
+
+
+class SclkSampler:
+    """Polls the GPU's current shader clock from sysfs on a host thread while
+    the GPU runs (hwmon freq1_input, else the active level of pp_dpm_sclk of
+    the PCI device torch reports for cuda:0).  Reports null with the reason
+    when neither file is readable."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        import torch
+        self.period = period_s
+        self.samples = []
+        self.path, self.kind, self.reason = None, None, None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            dev = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
+            hw = sorted(glob.glob(dev + "/hwmon/hwmon*/freq1_input"))
+            if hw and os.access(hw[0], os.R_OK):
+                self.path, self.kind = hw[0], "hwmon freq1_input"
+            elif os.access(dev + "/pp_dpm_sclk", os.R_OK):
+                self.path, self.kind = dev + "/pp_dpm_sclk", "pp_dpm_sclk active level"
+            else:
+                self.reason = f"no readable clock file under {dev}"
+        except Exception as e:  # noqa: BLE001 - reported, never fatal
+            self.reason = f"{type(e).__name__}: {e}"
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read_mhz(self):
+        with open(self.path) as f:
+            text = f.read()
+        if self.kind.startswith("hwmon"):
+            return int(text.strip()) / 1e6
+        for line in text.splitlines():
+            if line.strip().endswith("*"):
+                return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read_mhz()
+                if v:
+                    self.samples.append(v)
+            except Exception as e:  # noqa: BLE001
+                self.reason = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def report(self) -> dict:
+        if not self.samples:
+            return {"mhz_mean": None, "source": self.kind, "note": self.reason or "no samples"}
+        a = np.asarray(self.samples)
+        return {"mhz_mean": round(float(a.mean()), 1), "mhz_min": round(float(a.min()), 1),
+                "mhz_max": round(float(a.max()), 1), "samples": int(a.size), "source": self.kind,
+                "window": "warm-up and timed rings"}
+
+
+def host_info() -> dict:
+    """The host the oracle runs on: `cores` is the thread count the oracle
+    actually uses for its products (numpy's BLAS threads; the exponentials run
+    on one thread), `affinity_cores` the CPUs this process may run on
+    (os.sched_getaffinity), plus the CPU model and the BLAS library."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas, blas_threads = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')}"
+            blas_threads = max(i.get("num_threads", 1) for i in libs)
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cores": blas_threads, "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": model, "blas": blas}
+
+
 def timed_rings(args) -> int:
     """Timed rings whose step launches carry timing events (every time_every-th)."""
     return (args.steps + args.time_every - 1) // args.time_every
@@ -109,12 +219,7 @@ def cpu_baseline(wl, rank, blocks, target_s=15.0):
     """The CPU fp64 oracle, as it stands, on a bounded sample of query rows."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _helpers import oracle_rank          # test plumbing around oracle/
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas")
-    except Exception:
-        blas_threads = None
+    host = host_info()
     cache = dict(blocks)
     kv_blocks = list(range(rank + 1)) if wl.causal else list(range(wl.blocks))
     n = 4
@@ -127,8 +232,8 @@ def cpu_baseline(wl, rank, blocks, target_s=15.0):
             break
         n = min(wl.rows, int(n * max(2.0, target_s / 3 / max(dt, 1e-3))))
     flops = 4 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank, rows)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
-            "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host["cores"],
+            "kind": "oracle", **{k: v for k, v in host.items() if k != "cores"},
             "sample": f"{len(rows)} seeded query rows x {wl.heads} heads of rank {rank} "
                       f"({flops / 1e9:.1f} GFLOP fp64, {dt:.1f} s; numpy BLAS threads for the "
                       f"products, one thread for exp)"}
@@ -142,12 +247,7 @@ def cpu_baseline_decode(wl, blocks, rq, target_s=15.0):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _helpers import oracle_values        # test plumbing around oracle/
     from oracle import dense
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas")
-    except Exception:
-        blas_threads = None
+    host = host_info()
     P, c = wl.blocks, wl.rows
     qh = synth.block(wl, synth.ROLE_Q, P, rows=rq)
     kp, qp = np.arange(P * c), np.full(rq, P * c)
@@ -165,7 +265,8 @@ def cpu_baseline_decode(wl, blocks, rq, target_s=15.0):
             break
     dt = time.perf_counter() - t0
     nbytes = 2 * P * c * wl.head_dim * esize * done
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": host["cores"], "kind": "oracle",
+            **{k: v for k, v in host.items() if k != "cores"},
             "sample": f"{rq} query rows x {done} of {wl.heads} heads against {P} x {c} keys "
                       f"({nbytes / 1e6:.0f} MB of keys and values, {dt:.1f} s; numpy BLAS threads "
                       f"for the products, one thread for exp)"}
@@ -197,25 +298,26 @@ def bench_decode(args, wl):
     dec = ChunkedDecode(q.shape, P, dev, compute_stream=compute)
     o = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
-    torch.cuda.synchronize()
     # The step kernel of one timed step in time_every carries timing events
     # bound to its dispatch.
     n_timed = len(range(0, args.steps, args.time_every))
     pool = iter([Event(timing=True) for _ in range(2 * n_timed)])
     timers = []
     e0, e1 = Event(timing=True), Event(timing=True)
-    t0 = time.perf_counter()
-    e0.record(compute)
-    for s in range(args.steps):
-        ev = (next(pool), next(pool)) if s % args.time_every == 0 else (None, None)
-        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse, start=ev[0], stop=ev[1])
-        if ev[0] is not None:
-            timers.append(ev)
-    e1.record(compute)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        for _ in range(args.warmup):
+            dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(compute)
+        for s in range(args.steps):
+            ev = (next(pool), next(pool)) if s % args.time_every == 0 else (None, None)
+            dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse, start=ev[0], stop=ev[1])
+            if ev[0] is not None:
+                timers.append(ev)
+        e1.record(compute)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
     esize = 2 if wl.dtype == "bf16" else 4
     kv_bytes = 2 * P * c * wl.heads * wl.head_dim * esize
@@ -247,6 +349,8 @@ def bench_decode(args, wl):
                      "avg_launch_ms": round(step_ms, 5), "launches": len(timers),
                      "timed_steps": f"1 in {args.time_every} of the {args.steps} timed steps"},
         "compute_stream_ms": round(e0.elapsed_time(e1) / args.steps, 4),
+        "sclk": sclk.report(),
+        "env": software_versions(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(wl, blocks, rq)
@@ -261,12 +365,7 @@ def cpu_baseline_backward(wl, rank, blocks, target_s=15.0):
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _helpers import oracle_values        # test plumbing around oracle/
     from oracle import backward, dense
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max(i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas")
-    except Exception:
-        blas_threads = None
+    host = host_info()
     kv_blocks = list(range(rank + 1)) if wl.causal else list(range(wl.blocks))
     kp = np.concatenate([dense.ring_positions(j, wl.rows) for j in kv_blocks])
     n = 4
@@ -288,8 +387,8 @@ def cpu_baseline_backward(wl, rank, blocks, target_s=15.0):
             break
         n = min(wl.rows, int(n * max(2.0, target_s / 3 / max(dt, 1e-3))))
     flops = 10 * wl.head_dim * wl.heads * unmasked_pairs(wl, rank, rows)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads,
-            "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": host["cores"],
+            "kind": "oracle", **{k: v for k, v in host.items() if k != "cores"},
             "sample": f"{len(rows)} seeded query rows x {wl.heads} heads of rank {rank}, backward "
                       f"({flops / 1e9:.1f} GFLOP fp64, {dt:.1f} s; numpy BLAS threads for the "
                       f"products, one thread for exp)"}
@@ -361,17 +460,18 @@ def bench_backward(args, wl, rank):
             ring.run_backward(qs[0], dos[0], lses[0], deltas[0], dqs[0], source, rank, wl.blocks,
                               wl.causal, wl.scale, step_timers=timers, timer_events=pool)
 
-    for _ in range(args.warmup):
-        one_ring()
-    torch.cuda.synchronize()
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
     pool = iter([Event(timing=True) for _ in range(2 * launched * timed_rings(args))])
     timers = []
-    t0 = time.perf_counter()
-    for r in range(args.steps):
-        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        for _ in range(args.warmup):
+            one_ring()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for r in range(args.steps):
+            one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
     c2 = step_wl.rows
     pairs = (cases.count(_lib.RA_CASE_FULL) * c2 * c2 + cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
@@ -409,6 +509,11 @@ def bench_backward(args, wl, rank):
                      "launches": len(full) if full else len(diag),
                      "timed_rings": f"1 in {args.time_every} of the {args.steps} timed rings",
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
+        "ring": {"cases": {"skip": cases.count(_lib.RA_CASE_SKIP),
+                           "diag": cases.count(_lib.RA_CASE_DIAG),
+                           "full": cases.count(_lib.RA_CASE_FULL)}},
+        "sclk": sclk.report(),
+        "env": software_versions(),
     }
     if not args.no_cpu_baseline and not zigzag:
         line["cpu_baseline"] = cpu_baseline_backward(wl, rank, blocks)
@@ -538,20 +643,20 @@ def main():
             for st, (o_out, lse_out) in zip(states, outs):
                 _lib.finalize(st, stream=compute, o_out=o_out, lse_out=lse_out)
 
-    for _ in range(args.warmup):
-        one_ring()
-    torch.cuda.synchronize()
-
     # Timing events for every launched step of the sampled timed rings,
     # created before the timed region.
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
     pool = iter([Event(timing=True) for _ in range(2 * launched * timed_rings(args))])
     timers = []
-    t0 = time.perf_counter()
-    for r in range(args.steps):
-        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        for _ in range(args.warmup):
+            one_ring()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for r in range(args.steps):
+            one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
 
     ms = elapsed / args.steps * 1e3
     tflops = flops / (ms / 1e3) / 1e12
@@ -566,6 +671,12 @@ def main():
         dom = "ra_step diagonal"
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_VECTOR_TFLOPS
     achieved = dom_flops / (dom_ms / 1e3) / 1e12
+    n_full, n_diag = cases.count(_lib.RA_CASE_FULL), cases.count(_lib.RA_CASE_DIAG)
+    kernel_ms = n_full * (float(np.mean(full)) if full else 0.0) + \
+        n_diag * (float(np.mean(diag)) if diag else 0.0)
+    esize = 2 if wl.dtype == "bf16" else 4
+    per_visit = 2 if args.partition == "contiguous" else 4
+    staged = (wl.blocks - 1) * per_visit * wl.heads * step_wl.rows * wl.head_dim * esize
 
     line = {
         "metric": (f"{'causal' if wl.causal else 'non-causal'} {wl.dtype} ring-step attention "
@@ -596,6 +707,15 @@ def main():
                      "launches": len(full) if full else len(diag),
                      "timed_rings": f"1 in {args.time_every} of the {args.steps} timed rings",
                      "diag_avg_launch_ms": round(float(np.mean(diag)), 5) if diag else None},
+        "ring": {"cases": {"skip": cases.count(_lib.RA_CASE_SKIP), "diag": n_diag, "full": n_full},
+                 "step_kernel_ms": round(kernel_ms, 5),
+                 "exposed_ms": round(ms - kernel_ms, 5),
+                 "exposed_note": "ring time minus the step kernels' event-timed average durations: "
+                                 "launch gaps and cross-stream waits on the compute stream",
+                 "bytes_staged": staged,
+                 "staged_GBps": round(staged / (ms / 1e3) / 1e9, 1)},
+        "sclk": sclk.report(),
+        "env": software_versions(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step_wl, baseline_q, blocks)

@@ -33,6 +33,10 @@
  *     failed to enqueue.  No exception or abort crosses this boundary.
  *   - Calls that share a state or an output must not overlap on different
  *     streams unless the caller orders them with events.
+ *   - Within one call, every buffer the call writes (state m, l, o; outputs;
+ *     gradients) must be disjoint from every other buffer the call names, and
+ *     a state's m, l and o from each other.  Overlapping byte ranges are
+ *     rejected with RA_ERR_INVALID_ARG before anything is enqueued.
  */
 #ifndef RA_H_
 #define RA_H_
@@ -193,7 +197,7 @@ ra_status ra_step_timed(ra_state *st, const void *q, const void *k, const void *
  * (aicassindra architecture article, section "The architecture: every piece
  * explained": take the larger maximum, rescale each side by exp(its max - new
  * max), add).  Shapes must match.  A row empty on one side takes the other
- * side's values bit-exactly.  dst and src must not alias.
+ * side's values bit-exactly.  dst and src must not overlap.
  */
 ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream);
 

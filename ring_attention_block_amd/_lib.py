@@ -104,6 +104,52 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+_IO_DTYPES = (torch.float32, torch.bfloat16)
+_F32 = (torch.float32,)
+
+
+# Every wrapper below validates each caller-supplied tensor before any call
+# into the library, so a wrong buffer never reaches a kernel: first the layout
+# of every tensor (shape, dtype, contiguity), then that all of them are GPU
+# tensors (_on_gpu).
+
+def _check_buf(name: str, t, shape, dtypes) -> None:
+    """A tensor that a kernel reads or writes: contiguous, exactly `shape`,
+    one of `dtypes`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {[str(d) for d in dtypes]}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_input(name: str, t) -> None:
+    """A q, k, v, o or dout operand: contiguous (shapes and dtypes are checked
+    by the caller against the other operands)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors) -> None:
+    """Every named tensor (None: absent) lives in GPU memory."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+
+
+def _check_state(st: "State", name: str = "state") -> None:
+    b, h, r, d = st.shape
+    _check_buf(f"{name}.m", st.m, (b, h, r), _F32)
+    _check_buf(f"{name}.l", st.l, (b, h, r), _F32)
+    _check_buf(f"{name}.o", st.o, (b, h, r, d), _F32)
+    _on_gpu(**{f"{name}.m": st.m, f"{name}.l": st.l, f"{name}.o": st.o})
+
+
 def _event(ev) -> int | None:
     """A hipEvent_t from an event object with a .handle, a raw handle, or None."""
     if ev is None:
@@ -146,6 +192,7 @@ def step_case(q_block: int, kv_block: int, num_blocks: int, causal: bool) -> int
 
 
 def state_init(st: State, stream=None) -> None:
+    _check_state(st)
     _check(lib().ra_state_init(ctypes.byref(st.c), _stream(stream)))
 
 
@@ -172,8 +219,7 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
     begin and end of the step kernel's dispatch.
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+        _check_input(name, t)
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k and v must share one dtype")
     q_batch = 1 if flags & RA_STEP_Q_BROADCAST else k.shape[0]
@@ -182,18 +228,19 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
         raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if (k.shape[0], *q.shape[1:]) != st.shape:
         raise ValueError(f"q shape {tuple(q.shape)} does not match the state {st.shape}")
+    b, h, r, d = st.shape
+    if flags & RA_STEP_FINALIZE:
+        if o_out is not None:
+            _check_buf("o_out", o_out, (b, h, r, d), _IO_DTYPES)
+        if lse_out is not None:
+            _check_buf("lse_out", lse_out, (b, h, r), _F32)
+    _on_gpu(q=q, k=k, v=v, o_out=o_out, lse_out=lse_out)
+    _check_state(st)
     if flags == 0 and start is None and stop is None:
         _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
                              k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
                              _stream(stream)))
     else:
-        b, h, r, d = st.shape
-        if o_out is not None and (tuple(o_out.shape) != (b, h, r, d) or not o_out.is_contiguous()
-                                  or o_out.dtype not in (torch.float32, torch.bfloat16)):
-            raise ValueError("o_out must be a contiguous fp32 or bf16 tensor of the state's shape")
-        if lse_out is not None and (tuple(lse_out.shape) != (b, h, r) or not lse_out.is_contiguous()
-                                    or lse_out.dtype != torch.float32):
-            raise ValueError("lse_out must be a contiguous fp32 [B,H,rows] tensor")
         out_code = RA_BF16 if o_out is not None and o_out.dtype == torch.bfloat16 else RA_F32
         args = (ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), k.shape[2], q_block,
                 kv_block, num_blocks, int(causal), float(scale), int(flags), _ptr(o_out), out_code,
@@ -206,6 +253,8 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
 
 
 def lse_merge(dst: State, src: State, stream=None) -> None:
+    _check_state(dst, "dst")
+    _check_state(src, "src")
     _check(lib().ra_lse_merge(ctypes.byref(dst.c), ctypes.byref(src.c), _stream(stream)))
 
 
@@ -216,9 +265,11 @@ def finalize(st: State, out_dtype=torch.float32, stream=None, o_out=None, lse_ou
         o_out = torch.empty((b, h, r, d), dtype=out_dtype, device=st.o.device)
     if lse_out is None:
         lse_out = torch.empty((b, h, r), dtype=torch.float32, device=st.o.device)
+    _check_buf("o_out", o_out, (b, h, r, d), _IO_DTYPES)
+    _check_buf("lse_out", lse_out, (b, h, r), _F32)
+    _on_gpu(o_out=o_out, lse_out=lse_out)
+    _check_state(st)
     code = RA_BF16 if o_out.dtype == torch.bfloat16 else RA_F32
-    if o_out.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError(f"unsupported output dtype {o_out.dtype}")
     _check(lib().ra_finalize(ctypes.byref(st.c), _ptr(o_out), code, _ptr(lse_out), _stream(stream)))
     return o_out, lse_out
 
@@ -235,10 +286,10 @@ def merge_finalize(st: State, parts: int, out_dtype=torch.float32, stream=None, 
         o_out = torch.empty((b // parts, h, r, d), dtype=out_dtype, device=st.o.device)
     if lse_out is None:
         lse_out = torch.empty((b // parts, h, r), dtype=torch.float32, device=st.o.device)
-    if o_out.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError(f"unsupported output dtype {o_out.dtype}")
-    if tuple(o_out.shape) != (b // parts, h, r, d) or tuple(lse_out.shape) != (b // parts, h, r):
-        raise ValueError("merge_finalize: output shapes do not match the state")
+    _check_buf("o_out", o_out, (b // parts, h, r, d), _IO_DTYPES)
+    _check_buf("lse_out", lse_out, (b // parts, h, r), _F32)
+    _on_gpu(o_out=o_out, lse_out=lse_out)
+    _check_state(st)
     code = RA_BF16 if o_out.dtype == torch.bfloat16 else RA_F32
     _check(lib().ra_merge_finalize(ctypes.byref(st.c), int(parts), _ptr(o_out), code, _ptr(lse_out),
                                    _stream(stream)))
@@ -246,6 +297,9 @@ def merge_finalize(st: State, parts: int, out_dtype=torch.float32, stream=None, 
 
 
 def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    _check_input("dst", dst)
+    _check_input("src", src)
+    _on_gpu(dst=dst, src=src)
     if dst.numel() * dst.element_size() != src.numel() * src.element_size():
         raise ValueError("stage_block: sizes differ")
     _check(lib().ra_stage_block(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
@@ -256,16 +310,18 @@ def bwd_prepare(o, dout, delta=None, stream=None, dq=None):
     """delta = rowsum(dout * o) [B,H,rows] fp32 (o: the forward output); dq, if
     given (fp32, o's shape), is set to zero in the same launch."""
     for name, t in (("o", o), ("dout", dout)):
-        if not t.is_contiguous() or t.dim() != 4:
-            raise ValueError(f"{name} must be a contiguous [B,H,rows,d] tensor")
+        _check_input(name, t)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be a [B,H,rows,d] tensor")
     if o.shape != dout.shape:
         raise ValueError(f"o {tuple(o.shape)} and dout {tuple(dout.shape)} differ")
     b, h, r, d = o.shape
     if delta is None:
         delta = torch.empty((b, h, r), dtype=torch.float32, device=o.device)
-    if dq is not None and (tuple(dq.shape) != (b, h, r, d) or dq.dtype != torch.float32
-                           or not dq.is_contiguous()):
-        raise ValueError("dq must be a contiguous fp32 tensor of o's shape")
+    _check_buf("delta", delta, (b, h, r), _F32)
+    if dq is not None:
+        _check_buf("dq", dq, (b, h, r, d), _F32)
+    _on_gpu(o=o, dout=dout, delta=delta, dq=dq)
     _check(lib().ra_bwd_prepare(b, h, r, d, _ptr(o), _dtype_code(o), _ptr(dout), _dtype_code(dout),
                                 _ptr(delta), _ptr(dq), _stream(stream)))
     return delta
@@ -277,18 +333,17 @@ def bwd_step(q, dout, lse, delta, k, v, dq, dk, dv, q_block: int, kv_block: int,
     """Add block kv_block's backward contribution: dq += ..., dk += ..., dv += ...
     start, stop (ra_bwd_step_timed): timing events bound to the step's first
     and last kernel dispatch.  Returns the causal case."""
-    tensors = (("q", q), ("dout", dout), ("k", k), ("v", v), ("dq", dq), ("dk", dk), ("dv", dv))
-    for name, t in tensors:
-        if not t.is_contiguous() or tuple(t.shape) != tuple(q.shape):
-            raise ValueError(f"{name} must be contiguous with the shape of q {tuple(q.shape)}")
-    if not (q.dtype == dout.dtype == k.dtype == v.dtype):
-        raise TypeError("q, dout, k and v must share one dtype")
-    if not (dq.dtype == dk.dtype == dv.dtype == torch.float32):
-        raise TypeError("dq, dk and dv must be float32 accumulators")
+    _check_input("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be a [B,H,rows,d] tensor")
+    for name, t in (("dout", dout), ("k", k), ("v", v)):
+        _check_buf(name, t, q.shape, (q.dtype,))
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buf(name, t, q.shape, _F32)
     b, h, r, d = q.shape
     for name, t in (("lse", lse), ("delta", delta)):
-        if t.dtype != torch.float32 or tuple(t.shape) != (b, h, r) or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 [B,H,rows] tensor")
+        _check_buf(name, t, (b, h, r), _F32)
+    _on_gpu(q=q, dout=dout, lse=lse, delta=delta, k=k, v=v, dq=dq, dk=dk, dv=dv)
     args = (b, h, r, d, _ptr(q), _ptr(dout), _ptr(lse), _ptr(delta), _ptr(k), _ptr(v),
             _dtype_code(q), _ptr(dq), _ptr(dk), _ptr(dv), q_block, kv_block, num_blocks,
             int(causal), float(scale))

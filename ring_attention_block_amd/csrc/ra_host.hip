@@ -31,6 +31,19 @@ ra_status ok() {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
+// A byte range of one tensor argument, for the overlap checks.
+struct Span {
+  const void *p;
+  int64_t bytes;
+  const char *name;
+};
+
+bool overlap(const Span &a, const Span &b) {
+  if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+  return x < y + (uintptr_t)b.bytes && y < x + (uintptr_t)a.bytes;
+}
+
 // Rows of a state (batch * heads * rows) or -1 on a malformed shape.
 // Shape rules shared by every entry point: rows >= 0, head_dim 64 or 128, and
 // the row count bounded so that element offsets fit comfortably in 64 bits.
@@ -62,6 +75,12 @@ ra_status check_state(const ra_state *st, const char *name, int64_t *n_rows) {
       return fail(RA_ERR_INVALID_ARG, "%s: NULL m, l or o with %lld rows", name, (long long)n);
     if (!aligned4(st->m) || !aligned4(st->l) || !aligned16(st->o))
       return fail(RA_ERR_INVALID_ARG, "%s: o must be 16-byte aligned, m and l 4-byte aligned", name);
+    const Span parts[] = {{st->m, n * 4, "state m"}, {st->l, n * 4, "state l"},
+                          {st->o, n * st->head_dim * 4, "state o"}};
+    for (int i = 0; i < 3; ++i)
+      for (int j = i + 1; j < 3; ++j)
+        if (overlap(parts[i], parts[j]))
+          return fail(RA_ERR_INVALID_ARG, "%s: %s and %s overlap", name, parts[i].name, parts[j].name);
   }
   *n_rows = n;
   return RA_OK;
@@ -77,6 +96,22 @@ ra_status hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess)
     return fail(RA_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
   return ok();
+}
+
+// Every buffer a call writes must be disjoint from every other buffer it
+// touches (the kernels read and write through __restrict__ pointers, and
+// different workgroups own different rows, so any overlap is a race).
+template <size_t NW, size_t NR>
+ra_status check_disjoint(const char *name, const Span (&w)[NW], const Span (&r)[NR]) {
+  for (size_t i = 0; i < NW; ++i) {
+    for (size_t j = i + 1; j < NW; ++j)
+      if (overlap(w[i], w[j]))
+        return fail(RA_ERR_INVALID_ARG, "%s: %s and %s overlap", name, w[i].name, w[j].name);
+    for (size_t j = 0; j < NR; ++j)
+      if (overlap(w[i], r[j]))
+        return fail(RA_ERR_INVALID_ARG, "%s: %s and %s overlap", name, w[i].name, r[j].name);
+  }
+  return RA_OK;
 }
 
 }  // namespace
@@ -160,6 +195,21 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
       if (!aligned16(k) || !aligned16(v))
         return fail(RA_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", name);
     }
+    const int64_t es = in_dtype == RA_BF16 ? 2 : 4, d = st->head_dim;
+    const int64_t q_rows = (flags & RA_STEP_Q_BROADCAST) ? (int64_t)st->heads * st->rows : n;
+    const int64_t kv_n = (int64_t)st->batch * st->heads * kv_rows;
+    const Span in[] = {{q, q_rows * d * es, "q"}, {k, kv_n * d * es, "k"}, {v, kv_n * d * es, "v"}};
+    const Span state[] = {{st->m, n * 4, "state m"}, {st->l, n * 4, "state l"},
+                          {st->o, n * d * 4, "state o"}};
+    if (flags & RA_STEP_FINALIZE) {
+      const Span out[] = {{o_out, n * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"},
+                          {lse_out, n * 4, "lse_out"}};
+      const Span rd[] = {in[0], in[1], in[2], state[0], state[1], state[2]};
+      s = check_disjoint(name, out, rd);
+    } else {
+      s = check_disjoint(name, state, in);
+    }
+    if (s != RA_OK) return s;
   }
   if (n == 0 || c == RA_CASE_SKIP || kv_rows == 0) {
     // Nothing to fold: the flags still take effect through the state kernels,
@@ -245,8 +295,11 @@ ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream) {
       dst->head_dim != src->head_dim)
     return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: dst and src shapes differ");
   if (nd == 0) return ok();
-  if (dst->m == src->m || dst->l == src->l || dst->o == src->o)
-    return fail(RA_ERR_INVALID_ARG, "ra_lse_merge: dst and src alias");
+  const int64_t d = dst->head_dim;
+  const Span w[] = {{dst->m, nd * 4, "dst m"}, {dst->l, nd * 4, "dst l"}, {dst->o, nd * d * 4, "dst o"}};
+  const Span r[] = {{src->m, ns * 4, "src m"}, {src->l, ns * 4, "src l"}, {src->o, ns * d * 4, "src o"}};
+  s = check_disjoint("ra_lse_merge", w, r);
+  if (s != RA_OK) return s;
   (void)hipGetLastError();
   return hip_status(ra::launch_state_merge(dst->m, dst->l, dst->o, src->m, src->l, src->o, nd,
                                            dst->head_dim, stream),
@@ -264,6 +317,13 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
   if (n == 0 || (!o_out && !lse_out)) return ok();
   if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
     return fail(RA_ERR_INVALID_ARG, "ra_finalize: outputs must be 16-byte aligned");
+  {
+    const int64_t d = st->head_dim;
+    const Span w[] = {{o_out, n * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"}, {lse_out, n * 4, "lse_out"}};
+    const Span r[] = {{st->m, n * 4, "state m"}, {st->l, n * 4, "state l"}, {st->o, n * d * 4, "state o"}};
+    s = check_disjoint("ra_finalize", w, r);
+    if (s != RA_OK) return s;
+  }
   (void)hipGetLastError();
   return hip_status(ra::launch_finalize(st->m, st->l, st->o, o_out, out_dtype == RA_BF16,
                                         lse_out, n, st->head_dim, stream),
@@ -284,6 +344,13 @@ ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_d
   if (n == 0 || (!o_out && !lse_out)) return ok();
   if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
     return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: outputs must be 16-byte aligned");
+  {
+    const int64_t d = st->head_dim, no = n / parts;
+    const Span w[] = {{o_out, no * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"}, {lse_out, no * 4, "lse_out"}};
+    const Span r[] = {{st->m, n * 4, "state m"}, {st->l, n * 4, "state l"}, {st->o, n * d * 4, "state o"}};
+    s = check_disjoint("ra_merge_finalize", w, r);
+    if (s != RA_OK) return s;
+  }
   const int64_t hr = (int64_t)st->heads * st->rows;
   (void)hipGetLastError();
   return hip_status(ra::launch_merge_finalize(st->m, st->l, st->o, o_out, out_dtype == RA_BF16,
@@ -303,9 +370,17 @@ ra_status ra_bwd_prepare(int32_t batch, int32_t heads, int32_t rows, int32_t hea
   if (!o || !dout || !delta || !aligned16(o) || !aligned16(dout) || !aligned16(delta))
     return fail(RA_ERR_INVALID_ARG,
                 "ra_bwd_prepare: o, dout and delta must be non-NULL and 16-byte aligned");
-  (void)hipGetLastError();
   if (dq && !aligned16(dq))
     return fail(RA_ERR_INVALID_ARG, "ra_bwd_prepare: dq must be 16-byte aligned");
+  {
+    const int64_t d = head_dim;
+    const Span w[] = {{delta, n * 4, "delta"}, {dq, n * d * 4, "dq"}};
+    const Span r[] = {{o, n * d * (o_dtype == RA_BF16 ? 2 : 4), "o"},
+                      {dout, n * d * (do_dtype == RA_BF16 ? 2 : 4), "dout"}};
+    s = check_disjoint("ra_bwd_prepare", w, r);
+    if (s != RA_OK) return s;
+  }
+  (void)hipGetLastError();
   return hip_status(ra::launch_bwd_prepare(o, o_dtype == RA_BF16, dout, do_dtype == RA_BF16, delta,
                                            dq, n, head_dim, stream),
                     "ra_bwd_prepare launch");
@@ -334,6 +409,12 @@ static ra_status bwd_impl(const char *name, int32_t batch, int32_t heads, int32_
       if (!p || !aligned16(p))
         return fail(RA_ERR_INVALID_ARG,
                     "%s: q, dout, lse, delta, k, v, dq, dk, dv must be non-NULL and 16-byte aligned", name);
+    const int64_t d = head_dim, es = in_dtype == RA_BF16 ? 2 : 4;
+    const Span w[] = {{dq, n * d * 4, "dq"}, {dk, n * d * 4, "dk"}, {dv, n * d * 4, "dv"}};
+    const Span r[] = {{q, n * d * es, "q"}, {dout, n * d * es, "dout"}, {lse, n * 4, "lse"},
+                      {delta, n * 4, "delta"}, {k, n * d * es, "k"}, {v, n * d * es, "v"}};
+    s = check_disjoint(name, w, r);
+    if (s != RA_OK) return s;
   }
   if (c == RA_CASE_SKIP || n == 0) {
     // Nothing to add: the timing events are recorded back to back.

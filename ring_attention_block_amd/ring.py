@@ -83,6 +83,11 @@ class RingEmulator:
         self.ev_free = [Event(), Event()]
         self.ev_start = Event()
         self.last_stop = None
+        # free_hook(tensors, copy_stream), if set, is enqueued on the copy
+        # stream each time a receive buffer is released: after the stream has
+        # waited for the buffer's free event (and after the drain), before the
+        # next block is staged into it.  Tests poison released buffers with it.
+        self.free_hook = None
 
     def visit(self, order: Sequence[int], source: Callable[[int], tuple],
               fold: Callable[[int, int, tuple], None], drain=None) -> None:
@@ -124,6 +129,8 @@ class RingEmulator:
                     self.ev_free[cur_buf].wait(copy)
                 if drain is not None:
                     drain(j, cur, copy)
+                if self.free_hook is not None:
+                    self.free_hook(cur, copy)
             if nxt_buf is not None:
                 # The buffer just computed on becomes the next receive target;
                 # the copy stream has waited for its free event before refilling it.

@@ -34,6 +34,11 @@ class Workload:
     causal: bool
     ranks: tuple         # ranks emulated for this workload
     rescale_stress: bool = False
+    # Extreme scores: every scaled score against key `spike_key` (-1: every key)
+    # of each block in `spike_blocks` is offset by `spike` (see block_f32).
+    spike: float = 0.0
+    spike_blocks: tuple = ()
+    spike_key: int = -1
     note: str = field(default="", compare=False)
 
     @property
@@ -96,15 +101,26 @@ def block_f32(wl: Workload, role: int, block: int, rows: int | None = None,
     coordinate mean exactly 1 (so q . 1 = head_dim) and key block j is shifted
     by 2j/sqrt(head_dim) along the all-ones direction, which adds 2j to every
     scaled score against block j (up to the later bf16 rounding).
+
+    Extreme-score workloads (spike != 0) re-centre the query rows the same way
+    and shift key `spike_key` (every key if -1) of each block in spike_blocks
+    by spike/sqrt(head_dim) along the all-ones direction, which offsets every
+    scaled score against those keys by `spike` (up to the bf16 rounding).
     """
     rows = wl.rows if rows is None else rows
     heads = wl.heads if heads is None else heads
     z = normal_block(wl.seed, role, block, heads, rows, wl.head_dim)
-    if wl.rescale_stress:
+    if wl.rescale_stress or wl.spike:
         if role == ROLE_Q:
             z = z - z.mean(axis=2, keepdims=True, dtype=np.float64).astype(np.float32) + 1.0
-        elif role == ROLE_K:
+        elif role == ROLE_K and wl.rescale_stress:
             z = z + np.float32(2.0 * block / math.sqrt(wl.head_dim))
+        elif role == ROLE_K and block in wl.spike_blocks:
+            shift = np.float32(wl.spike / math.sqrt(wl.head_dim))
+            if wl.spike_key < 0:
+                z = z + shift
+            elif wl.spike_key < rows:
+                z[:, wl.spike_key, :] += shift
     return np.ascontiguousarray(z, dtype=np.float32)
 
 
