@@ -91,72 +91,46 @@ def software_versions() -> dict:
             "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
 
 
-class SclkSampler:
-    """Polls the GPU's current shader clock from sysfs on a host thread while
-    the GPU runs (hwmon freq1_input, else the active level of pp_dpm_sclk of
-    the PCI device torch reports for cuda:0).  Reports null with the reason
-    when neither file is readable."""
+COUNTER_PROFILE = "ra_step_bf16_causal_h32_d128_c4096_counters.md"
+COUNTER_KEYS = ("sclk_mhz", "mfma_busy_pct", "valu_busy_pct", "lds_bank_conflict_pct")
 
-    def __init__(self, period_s=0.002):
-        import glob
-        import threading
-        import torch
-        self.period = period_s
-        self.samples = []
-        self.path, self.kind, self.reason = None, None, None
-        try:
-            p = torch.cuda.get_device_properties(0)
-            dev = f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}.0"
-            hw = sorted(glob.glob(dev + "/hwmon/hwmon*/freq1_input"))
-            if hw and os.access(hw[0], os.R_OK):
-                self.path, self.kind = hw[0], "hwmon freq1_input"
-            elif os.access(dev + "/pp_dpm_sclk", os.R_OK):
-                self.path, self.kind = dev + "/pp_dpm_sclk", "pp_dpm_sclk active level"
-            else:
-                self.reason = f"no readable clock file under {dev}"
-        except Exception as e:  # noqa: BLE001 - reported, never fatal
-            self.reason = f"{type(e).__name__}: {e}"
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
 
-    def _read_mhz(self):
-        with open(self.path) as f:
-            text = f.read()
-        if self.kind.startswith("hwmon"):
-            return int(text.strip()) / 1e6
-        for line in text.splitlines():
-            if line.strip().endswith("*"):
-                return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+def profile_fields(name, keys):
+    """Machine-readable `key: value` lines of profiles/<name>, only while the
+    kernel source still hashes to the recorded kernel_source_sha256; else None."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
         return None
+    fields = {}
+    for line in open(path):
+        key, sep, val = line.strip().partition(": ")
+        if sep and (key in keys or key in ("kernel_source", "kernel_source_sha256")):
+            fields[key] = val.strip()
+    if "kernel_source" not in fields or "kernel_source_sha256" not in fields:
+        return None
+    src = os.path.join(ROOT, fields["kernel_source"])
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != fields["kernel_source_sha256"]:
+            return None
+    return fields
 
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                v = self._read_mhz()
-                if v:
-                    self.samples.append(v)
-            except Exception as e:  # noqa: BLE001
-                self.reason = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period)
 
-    def __enter__(self):
-        if self.path:
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread.is_alive():
-            self._thread.join()
-
-    def report(self) -> dict:
-        if not self.samples:
-            return {"mhz_mean": None, "source": self.kind, "note": self.reason or "no samples"}
-        a = np.asarray(self.samples)
-        return {"mhz_mean": round(float(a.mean()), 1), "mhz_min": round(float(a.min()), 1),
-                "mhz_max": round(float(a.max()), 1), "samples": int(a.size), "source": self.kind,
-                "window": "warm-up and timed rings"}
+def measured_counters(case):
+    """Shader clock and MFMA, VALU and LDS-conflict occupancy of the full
+    ("full") or diagonal ("diag") step kernel of the headline ring, from the
+    committed counter summary; `current` false (no figures) once the kernel
+    source has changed since the counters were taken."""
+    keys = tuple(f"{case}.{k}" for k in COUNTER_KEYS)
+    f = profile_fields(COUNTER_PROFILE, keys)
+    if not f:
+        return {"profile": "profiles/" + COUNTER_PROFILE, "current": False}
+    out = {"profile": "profiles/" + COUNTER_PROFILE, "current": True}
+    for k in COUNTER_KEYS:
+        v = f.get(f"{case}.{k}")
+        out[k] = float(v) if v else None
+    return out
 
 
 def host_info() -> dict:
@@ -197,22 +171,12 @@ def measured_traffic(wl, profile=TRAFFIC_PROFILE):
     Only for the workload the counters were taken on, and only while the
     kernel source still hashes to the value recorded with them; else None.
     """
-    if wl.name != DEFAULT_WORKLOAD or not os.path.exists(profile):
+    if wl.name != DEFAULT_WORKLOAD:
         return None
-    fields = {}
-    for line in open(profile):
-        key, sep, val = line.strip().partition(": ")
-        if sep and key in ("traffic_bytes_per_launch", "kernel_source", "kernel_source_sha256"):
-            fields[key] = val.strip()
-    if len(fields) != 3:
+    f = profile_fields(os.path.basename(profile), ("traffic_bytes_per_launch",))
+    if not f or "traffic_bytes_per_launch" not in f:
         return None
-    src = os.path.join(ROOT, fields["kernel_source"])
-    if not os.path.exists(src):
-        return None
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != fields["kernel_source_sha256"]:
-            return None
-    return int(fields["traffic_bytes_per_launch"])
+    return int(f["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, rank, blocks, target_s=15.0):
@@ -304,20 +268,19 @@ def bench_decode(args, wl):
     pool = iter([Event(timing=True) for _ in range(2 * n_timed)])
     timers = []
     e0, e1 = Event(timing=True), Event(timing=True)
-    with SclkSampler() as sclk:
-        for _ in range(args.warmup):
-            dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(compute)
-        for s in range(args.steps):
-            ev = (next(pool), next(pool)) if s % args.time_every == 0 else (None, None)
-            dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse, start=ev[0], stop=ev[1])
-            if ev[0] is not None:
-                timers.append(ev)
-        e1.record(compute)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+    for _ in range(args.warmup):
+        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(compute)
+    for s in range(args.steps):
+        ev = (next(pool), next(pool)) if s % args.time_every == 0 else (None, None)
+        dec.run(q, k, v, wl.scale, o_out=o, lse_out=lse, start=ev[0], stop=ev[1])
+        if ev[0] is not None:
+            timers.append(ev)
+    e1.record(compute)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
     esize = 2 if wl.dtype == "bf16" else 4
     kv_bytes = 2 * P * c * wl.heads * wl.head_dim * esize
@@ -349,7 +312,6 @@ def bench_decode(args, wl):
                      "avg_launch_ms": round(step_ms, 5), "launches": len(timers),
                      "timed_steps": f"1 in {args.time_every} of the {args.steps} timed steps"},
         "compute_stream_ms": round(e0.elapsed_time(e1) / args.steps, 4),
-        "sclk": sclk.report(),
         "env": software_versions(),
     }
     if not args.no_cpu_baseline:
@@ -463,15 +425,14 @@ def bench_backward(args, wl, rank):
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
     pool = iter([Event(timing=True) for _ in range(2 * launched * timed_rings(args))])
     timers = []
-    with SclkSampler() as sclk:
-        for _ in range(args.warmup):
-            one_ring()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for r in range(args.steps):
-            one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+    for _ in range(args.warmup):
+        one_ring()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     ms = elapsed / args.steps * 1e3
     c2 = step_wl.rows
     pairs = (cases.count(_lib.RA_CASE_FULL) * c2 * c2 + cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
@@ -512,7 +473,6 @@ def bench_backward(args, wl, rank):
         "ring": {"cases": {"skip": cases.count(_lib.RA_CASE_SKIP),
                            "diag": cases.count(_lib.RA_CASE_DIAG),
                            "full": cases.count(_lib.RA_CASE_FULL)}},
-        "sclk": sclk.report(),
         "env": software_versions(),
     }
     if not args.no_cpu_baseline and not zigzag:
@@ -528,9 +488,11 @@ def main():
     # rings of the 32-head causal workload ran 1-2% slower.
     ap.add_argument("--warmup", type=int, default=30)
     # Each timing event costs the compute stream a few microseconds between two
-    # step kernels, so the kernel durations are sampled: the launches of every
-    # K-th timed ring carry events (all rings with K = 1).
-    ap.add_argument("--time-every", type=int, default=4)
+    # step kernels (a bound start event about 8 us, a stop event about 4 us), so
+    # the kernel durations are sampled: the launches of every K-th timed ring
+    # carry events (all rings with K = 1).  At the defaults two of the 20 timed
+    # rings are sampled (14 full-step launches of the headline ring).
+    ap.add_argument("--time-every", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--partition", default="contiguous", choices=("contiguous", "zigzag"),
@@ -648,15 +610,14 @@ def main():
     launched = sum(c != _lib.RA_CASE_SKIP for c in cases)
     pool = iter([Event(timing=True) for _ in range(2 * launched * timed_rings(args))])
     timers = []
-    with SclkSampler() as sclk:
-        for _ in range(args.warmup):
-            one_ring()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for r in range(args.steps):
-            one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
+    for _ in range(args.warmup):
+        one_ring()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
 
     ms = elapsed / args.steps * 1e3
     tflops = flops / (ms / 1e3) / 1e12
@@ -714,7 +675,8 @@ def main():
                                  "launch gaps and cross-stream waits on the compute stream",
                  "bytes_staged": staged,
                  "staged_GBps": round(staged / (ms / 1e3) / 1e9, 1)},
-        "sclk": sclk.report(),
+        "counters": ({"full": measured_counters("full"), "diag": measured_counters("diag")}
+                     if wl.name == DEFAULT_WORKLOAD and args.partition == "contiguous" else None),
         "env": software_versions(),
     }
     if not args.no_cpu_baseline:
