@@ -409,12 +409,17 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     return (kDiag && t * kBN + kBN - 1 > q0w) || (t * kBN + kBN > kv_rows);
   };
 
-  // The O-state loads are issued last, before the first barrier, which waits
-  // only for the copies and the loads issued before them (vmcnt counts in
-  // issue order); they are first waited for at the P V product of tile 0.
-  // The scheduling barrier keeps every earlier load ahead of them.
+  // The previous O state.  The state update is linear in it: the new O is
+  // exp2(m_state - m_ref) O_state + (the P V products relative to m_ref).
+  // Launches with the element mask load it into the accumulators up front:
+  // the loads are issued last before the first barrier, which waits only for
+  // the copies and the loads issued before them (vmcnt counts in issue
+  // order), and are first waited for at the P V product of tile 0 (the
+  // scheduling barrier keeps every earlier load ahead of them).  Unmasked
+  // launches start from zero and add the state after the last tile, whose
+  // iteration issues its loads (last_tile below): no tile waits for them.
   __builtin_amdgcn_sched_barrier(0);
-  {
+  auto load_state_o = [&](f32x4 (&ol)[kDB * 4]) {
 #pragma unroll
     for (int b = 0; b < kDB; ++b)
 #pragma unroll
@@ -422,21 +427,31 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
         const uint32_t off = ((uint32_t)row * D + (uint32_t)(b * 32 + g * 8 + h * 4)) * 4;
         // (Cast the whole vector: a scalar bit cast of one element of the
         // loaded vector was compiled as a cast of element 0.)
-        const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rso, off, 0, 0));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) oacc[b][4 * g + e] = x[e];
+        ol[b * 4 + g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rso, off, 0, 0));
       }
+  };
+  if constexpr (kMask) {
+    f32x4 ol[kDB * 4];
+    load_state_o(ol);
+#pragma unroll
+    for (int b = 0; b < kDB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[b][4 * g + e] = ol[b * 4 + g][e];
+    constexpr int kOLoads = kDB * 4;
+    __builtin_amdgcn_s_waitcnt((kOLoads & 15) | ((kOLoads >> 4) << 14) | (7 << 4));  // vmcnt(kOLoads) lgkmcnt(0)
+  } else {
+#pragma unroll
+    for (int b = 0; b < kDB; ++b) oacc[b] = f32x16{};
+    __builtin_amdgcn_s_waitcnt(0);
   }
-  constexpr int kOLoads = kDB * 4;
-  __builtin_amdgcn_s_waitcnt((kOLoads & 15) | ((kOLoads >> 4) << 14) | (7 << 4));  // vmcnt(kOLoads) lgkmcnt(0)
   __syncthreads();   // K(0), V(0), K(1) (and a zeroed tail) visible to all
-  {
-    const bool read_state = row_ok && !fresh;
-    const float m_state = read_state ? m_ld * kLog2e : -INFINITY;
-    rs.m_ref = m_state;
-    rs.m_run = m_state;
-    rs.l = (read_state && h == 0) ? l_ld : 0.f;
-  }
+  const bool read_state = row_ok && !fresh;
+  const float m_state = read_state ? m_ld * kLog2e : -INFINITY;   // base 2
+  rs.m_ref = m_state;
+  rs.m_run = m_state;
+  rs.l = (read_state && h == 0) ? l_ld : 0.f;
   // Software pipeline, one tile ahead.  Iteration t issues the copies of
   // K(t+2) and V(t+1), and in one branch-free block computes the scores of
   // tile t+1, the exponentials of tile t, the P V product of tile t and the
@@ -527,21 +542,47 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
     __syncthreads();
   };
 
+  // The last tile of an unmasked launch: no next tile to score and no copies.
+  // The O-state loads go out once the tile's exponentials have freed the
+  // score registers, ahead of its P V product; the state is added after it.
+  auto last_tile = [&](const char *v_src) {
+    bf16x8 pb[4];
+    if (wave_active) tile_exp(s_cur, rs, pb, sl2);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 ol[kDB * 4];
+    load_state_o(ol);
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave_active) accumulate(pb, v_src);
+    // m_ref only grows from m_state, so the factor is at most 1 (0 for an
+    // empty state, whose loads read zeros).
+    const float a_old = m_state == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_state - rs.m_ref);
+#pragma unroll
+    for (int b = 0; b < kDB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[b][4 * g + e] = fmaf(a_old, ol[b * 4 + g][e], oacc[b][4 * g + e]);
+  };
+
   using Fast = std::integral_constant<bool, true>;
   using Masked = std::integral_constant<bool, false>;
   int t = 0;
   if constexpr (!kMask) {
-    // Iteration 0 runs outside the loop, so that the O-state loads issued
-    // after the first barrier are first waited for at its P V product rather
-    // than before the loop (n_tiles >= 1: empty blocks launch nothing).
-    iteration(Fast{}, 0, lds_k0, lds_v1, lds_k1, lds_v0);
-    t = 1;
+    // Tiles 0 .. n_tiles-2 take the interleaved block (tile t uses K and V
+    // buffers t % 2), the last one last_tile (n_tiles >= 1: empty blocks
+    // launch nothing).
 #pragma clang loop unroll(disable)
-    for (; t + 1 < n_tiles; t += 2) {
-      iteration(Fast{}, t, lds_k1, lds_v0, lds_k0, lds_v1);
-      iteration(Fast{}, t + 1, lds_k0, lds_v1, lds_k1, lds_v0);
+    for (; t + 2 < n_tiles; t += 2) {
+      iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+      iteration(Fast{}, t + 1, lds_k1, lds_v0, lds_k0, lds_v1);
     }
-    if (t < n_tiles) iteration(Fast{}, t, lds_k1, lds_v0, lds_k0, lds_v1);
+    if (t + 1 < n_tiles) {
+      iteration(Fast{}, t, lds_k0, lds_v1, lds_k1, lds_v0);
+      ++t;
+    }
+    // One call site (two inlined copies raised the register count); no copy
+    // is in flight, so the selected buffer cannot alias one being written.
+    last_tile((t & 1) ? lds_v1 : lds_v0);
   } else {
     // head_dim 64, and 8-wavefront workgroups: the tiles before the first one
     // that needs the element mask (on the diagonal: keys before every row of
