@@ -253,6 +253,21 @@ ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_d
 ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream);
 
 /*
+ * ra_stage_block with flags.  RA_STAGE_ALONE: no step runs beside this copy
+ * (in a ring, the step it overlaps is a skipped causal block, "Ring
+ * Attention：把超长序列沿设备环流动", section "Causal Attention
+ * 让环不再完全对称": such a rank only forwards the block), so the copy takes a
+ * full-chip grid instead of the small one built to run beside a step; it
+ * still runs correctly beside a step, only slows it.  flags == 0 is
+ * ra_stage_block.  Other flag bits: RA_ERR_INVALID_ARG.  Same argument rules
+ * as ra_stage_block.
+ */
+typedef enum {
+  RA_STAGE_ALONE = 1 /* no step runs beside the copy: full-chip grid */
+} ra_stage_flags;
+ra_status ra_stage_block_ex(void *dst, const void *src, size_t bytes, uint32_t flags, hipStream_t stream);
+
+/*
  * Backward, per-row term ("Ring Attention：...", section "Backward 需要让梯度也
  * 沿环传播": gradients of every block interaction, probabilities recomputed
  * from the saved log-sum-exp):  delta[row] = sum_x dout[row][x] * o[row][x],

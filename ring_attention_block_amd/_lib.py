@@ -17,10 +17,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libra.so")
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_HIP = 0, -1, -2, -3
 RA_F32, RA_BF16 = 0, 1
 RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
+RA_STAGE_ALONE = 1
 
 # Every symbol include/ra.h declares.
 EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_step_timed", "ra_lse_merge",
-           "ra_finalize", "ra_merge_finalize", "ra_stage_block", "ra_bwd_prepare", "ra_bwd_step", "ra_bwd_step_timed",
+           "ra_finalize", "ra_merge_finalize", "ra_stage_block", "ra_stage_block_ex", "ra_bwd_prepare", "ra_bwd_step",
+           "ra_bwd_step_timed",
            "ra_status_string", "ra_last_error")
 
 
@@ -60,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
             "ra_merge_finalize": (ctypes.c_int, [sp, i32, vp, ctypes.c_int, vp, vp]),
             "ra_stage_block": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
+            "ra_stage_block_ex": (ctypes.c_int, [vp, vp, ctypes.c_size_t, ctypes.c_uint32, vp]),
             "ra_bwd_prepare": (ctypes.c_int, [i32, i32, i32, i32, vp, ctypes.c_int, vp, ctypes.c_int,
                                               vp, vp, vp]),
             "ra_bwd_step": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, ctypes.c_int,
@@ -296,14 +299,20 @@ def merge_finalize(st: State, parts: int, out_dtype=torch.float32, stream=None, 
     return o_out, lse_out
 
 
-def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None, alone: bool = False) -> None:
+    """Copy src into dst on `stream`; alone (ra_stage_block_ex with
+    RA_STAGE_ALONE): no step runs beside the copy, which then takes the whole
+    chip."""
     _check_input("dst", dst)
     _check_input("src", src)
     _on_gpu(dst=dst, src=src)
     if dst.numel() * dst.element_size() != src.numel() * src.element_size():
         raise ValueError("stage_block: sizes differ")
-    _check(lib().ra_stage_block(_ptr(dst), _ptr(src), src.numel() * src.element_size(),
-                                _stream(stream)))
+    n = src.numel() * src.element_size()
+    if alone:
+        _check(lib().ra_stage_block_ex(_ptr(dst), _ptr(src), n, RA_STAGE_ALONE, _stream(stream)))
+    else:
+        _check(lib().ra_stage_block(_ptr(dst), _ptr(src), n, _stream(stream)))
 
 
 def bwd_prepare(o, dout, delta=None, stream=None, dq=None):

@@ -471,16 +471,26 @@ ra_status ra_bwd_step_timed(int32_t batch, int32_t heads, int32_t rows, int32_t 
 
 
 
-ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+static ra_status stage_impl(const char *name, void *dst, const void *src, size_t bytes, uint32_t flags,
+                            hipStream_t stream) {
+  if (flags & ~(uint32_t)RA_STAGE_ALONE) return fail(RA_ERR_INVALID_ARG, "%s: unknown flags 0x%x", name, flags);
   if (bytes == 0) return ok();
-  if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "ra_stage_block: NULL pointer");
+  if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "%s: NULL pointer", name);
   const uintptr_t d = (uintptr_t)dst, s = (uintptr_t)src;
   if (d < s + bytes && s < d + bytes)
-    return fail(RA_ERR_INVALID_ARG, "ra_stage_block: source and destination overlap");
+    return fail(RA_ERR_INVALID_ARG, "%s: source and destination overlap", name);
   if (!aligned16(dst) || !aligned16(src) || bytes % 16 != 0)
-    return fail(RA_ERR_INVALID_ARG, "ra_stage_block: pointers must be 16-byte aligned and bytes a multiple of 16");
+    return fail(RA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned and bytes a multiple of 16", name);
   (void)hipGetLastError();
-  return hip_status(ra::launch_stage_copy(dst, src, bytes, stream), "ra_stage_block launch");
+  return hip_status(ra::launch_stage_copy(dst, src, bytes, (flags & RA_STAGE_ALONE) != 0, stream), name);
+}
+
+ra_status ra_stage_block(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+  return stage_impl("ra_stage_block", dst, src, bytes, 0, stream);
+}
+
+ra_status ra_stage_block_ex(void *dst, const void *src, size_t bytes, uint32_t flags, hipStream_t stream) {
+  return stage_impl("ra_stage_block_ex", dst, src, bytes, flags, stream);
 }
 
 }  // extern "C"

@@ -80,7 +80,7 @@ hipError_t launch_step_bf16(const StepArgs &a, int d, StepCase c, hipStream_t s,
 hipError_t launch_step_f32(const StepArgs &a, int d, StepCase c, hipStream_t s,
                            const LaunchTiming &t = {});
 // bytes a multiple of 16, both pointers 16-byte aligned, no overlap.
-hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s);
+hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, bool alone, hipStream_t s);
 hipError_t launch_bwd_prepare(const void *o, bool o_bf16, const void *dout, bool do_bf16,
                               float *delta, float *dq, int64_t n_rows, int d, hipStream_t s);
 hipError_t launch_bwd_step_simple(const BwdArgs &a, int d, bool bf16, StepCase c, hipStream_t s,

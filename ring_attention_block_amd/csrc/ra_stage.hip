@@ -17,6 +17,8 @@
 //   * non-temporal loads and stores (the block is not reused from cache by
 //     this copy).
 // A 32 MiB block then takes a few tens of microseconds, well inside one step.
+// A copy with no step beside it (the step it overlaps is a skipped causal
+// block) takes a full-chip grid instead: 8 workgroups per compute unit.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,6 +32,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 constexpr int kUnroll = 3;
 constexpr int64_t kMaxBlocks = 128;
+constexpr int64_t kMaxBlocksAlone = 2048;
 constexpr int64_t kMaxChunk = (int64_t)1 << 30;   // buffer offsets are 32-bit
 constexpr int kNonTemporal = 2;                    // buffer access cache policy: nt
 constexpr int kRawBuffer = 0x00020000;             // buffer resource: raw (untyped) 32-bit words
@@ -65,11 +68,12 @@ __global__ void __launch_bounds__(kThreads) stage_copy_kernel(char *__restrict__
 
 }  // namespace
 
-hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, hipStream_t s) {
+hipError_t launch_stage_copy(void *dst, const void *src, size_t bytes, bool alone, hipStream_t s) {
   const int64_t n = (int64_t)bytes;
   constexpr int64_t kPerRound = (int64_t)kThreads * 16 * kUnroll;
   int64_t blocks = (n + kPerRound - 1) / kPerRound;
-  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+  const int64_t max_blocks = alone ? kMaxBlocksAlone : kMaxBlocks;
+  if (blocks > max_blocks) blocks = max_blocks;
   const int64_t min_blocks = (n + kMaxChunk - 1) / kMaxChunk;
   if (blocks < min_blocks) blocks = min_blocks;
   if (blocks < 1) blocks = 1;

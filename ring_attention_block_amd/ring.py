@@ -90,7 +90,7 @@ class RingEmulator:
         self.free_hook = None
 
     def visit(self, order: Sequence[int], source: Callable[[int], tuple],
-              fold: Callable[[int, int, tuple], None], drain=None) -> None:
+              fold: Callable[[int, int, tuple], None], drain=None, busy=None) -> None:
         """The staging protocol: for each step s, fold(s, j, tensors) enqueues
         the compute on visiting rank j = order[s] on the compute stream while
         the tensors of order[s+1] are staged into the free buffer.
@@ -98,7 +98,11 @@ class RingEmulator:
         drain(j, tensors, stream), if given, is enqueued on the copy stream
         once the compute on a staged buffer has finished and before the buffer
         is refilled: the send of what the step updated (the backward's dK, dV)
-        to the next rank.  The compute stream waits for the last drain."""
+        to the next rank.  The compute stream waits for the last drain.
+
+        busy(s), if given, says whether step s launches any compute; the
+        staging that overlaps a step that does not (a skipped causal block)
+        runs alone and takes the whole chip (ra_stage_block_ex)."""
         comp, copy = self.compute, self.copy
         # Copies of this run start after everything already queued on the
         # compute stream (earlier runs may still read the buffers).
@@ -111,8 +115,9 @@ class RingEmulator:
             nxt_buf = None
             if s + 1 < len(order):
                 nxt_buf = free_buf
+                alone = busy is not None and not busy(s)
                 for dst, src in zip(self.bufs[nxt_buf], source(order[s + 1])):
-                    _lib.stage_block(dst, src, copy)
+                    _lib.stage_block(dst, src, copy, alone=alone)
                 self.ev_ready[nxt_buf].record(copy)
             if cur_buf is not None:
                 self.ev_ready[cur_buf].wait(comp)
@@ -201,7 +206,7 @@ class RingEmulator:
                       step_timers, timer_events, flags, finalize_out if flags else (None, None))
             cases.append(case)
 
-        self.visit(order, kv_source, fold)
+        self.visit(order, kv_source, fold, busy=lambda s: all_cases[s] != _lib.RA_CASE_SKIP)
         if finalize_out is not None and not fuse:
             _lib.finalize(st, stream=self.compute, o_out=finalize_out[0], lse_out=finalize_out[1])
         return cases
@@ -233,7 +238,8 @@ class RingEmulator:
             _lib.stage_block(dk, t[2], stream)
             _lib.stage_block(dv, t[3], stream)
 
-        self.visit(order, source, fold, drain)
+        self.visit(order, source, fold, drain,
+                   busy=lambda s: _lib.step_case(rank, order[s], num_blocks, causal) != _lib.RA_CASE_SKIP)
         return cases
 
 
@@ -289,7 +295,8 @@ class ZigzagRing:
                               2 * ranks, causal, scale, case, step_timers, timer_events, flags,
                               finalize_outs[a] if flags else (None, None))
 
-        self.emu.visit([j for j, _ in plan], kv_source, fold)
+        self.emu.visit([j for j, _ in plan], kv_source, fold,
+                       busy=lambda s: any(c != _lib.RA_CASE_SKIP for _, _, c in plan[s][1]))
         if finalize_outs is not None:
             for a, st in enumerate(states):
                 if not fuse[a]:
@@ -327,5 +334,6 @@ class ZigzagRing:
             for dst, src in zip(source(j)[4:8], t[4:8]):
                 _lib.stage_block(dst, src, stream)
 
-        self.emu.visit([j for j, _ in plan], source, fold, drain)
+        self.emu.visit([j for j, _ in plan], source, fold, drain,
+                       busy=lambda s: any(c != _lib.RA_CASE_SKIP for _, _, c in plan[s][1]))
         return plan

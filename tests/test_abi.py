@@ -146,6 +146,20 @@ def test_merge_finalize_stage_reject(L):
     assert L.ra_state_init(None, None) == _lib.RA_ERR_INVALID_ARG
 
 
+def test_stage_block_ex_rejects(L):
+    """ra_stage_block_ex: the same argument rules as ra_stage_block, and no
+    flag bit but RA_STAGE_ALONE."""
+    alone = _lib.RA_STAGE_ALONE
+    assert L.ra_stage_block_ex(None, None, 0, alone, None) == _lib.RA_OK
+    assert L.ra_stage_block_ex(FAKE, FAKE + 4096, 16, 2, None) == _lib.RA_ERR_INVALID_ARG
+    assert b"flags" in L.ra_last_error()
+    assert L.ra_stage_block_ex(FAKE, None, 16, alone, None) == _lib.RA_ERR_INVALID_ARG
+    assert L.ra_stage_block_ex(FAKE, FAKE + 8, 16, alone, None) == _lib.RA_ERR_INVALID_ARG
+    assert b"overlap" in L.ra_last_error()
+    assert L.ra_stage_block_ex(FAKE, FAKE + 4096, 24, alone, None) == _lib.RA_ERR_INVALID_ARG
+    assert b"aligned" in L.ra_last_error()
+
+
 BWD_NAMES = ("q", "dout", "lse", "delta", "k", "v", "dq", "dk", "dv")
 BWD_ADDR = {name: A(3 + n) for n, name in enumerate(BWD_NAMES)}
 

@@ -1,4 +1,4 @@
-"""GPU: the staging copy (ra_stage_block) moves exactly the bytes asked for.
+"""GPU: the staging copy (ra_stage_block, ra_stage_block_ex) moves exactly the bytes asked for.
 
 Byte-exact comparison on seeded random bytes, with guard regions around the
 destination that must stay untouched.  Sizes cover a copy shorter than one
@@ -27,10 +27,13 @@ def _gpu():
     _lib.lib()
 
 
+@pytest.mark.parametrize("alone", [False, True], ids=["beside_step", "alone"])
 @pytest.mark.parametrize("nbytes", [16, 4080, 12288, 12304, 1572864 + 16 * 7, 33554432,
                                     100 * 1048576 + 48])
-def test_stage_block_copies_exactly(nbytes):
-    print(f"  stage_block {nbytes} bytes", flush=True)
+def test_stage_block_copies_exactly(nbytes, alone):
+    """Both grids: the small one of ra_stage_block and the full-chip one of
+    ra_stage_block_ex with RA_STAGE_ALONE."""
+    print(f"  stage_block {nbytes} bytes alone={alone}", flush=True)
     sys.stdout.flush()
     rng = np.random.default_rng(nbytes)
     src_host = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
@@ -39,7 +42,7 @@ def test_stage_block_copies_exactly(nbytes):
     dst = dst_all[GUARD:GUARD + nbytes]
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
-    _lib.stage_block(dst, src, stream)
+    _lib.stage_block(dst, src, stream, alone=alone)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
     assert bool((dst_all[:GUARD] == 0xA5).all()) and bool((dst_all[GUARD + nbytes:] == 0xA5).all())
