@@ -508,6 +508,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="separate init and finalize launches instead of fusing them into the "
                          "first and last ring steps")
+    ap.add_argument("--key-split", default="auto", choices=("auto", "1", "2", "4"),
+                    help="key ranges per visiting block (no causal mask only): auto splits when "
+                         "the query block alone would leave compute units idle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.time_every < 1:
@@ -522,8 +525,8 @@ def main():
     import torch
     from ring_attention_block_amd import _lib
     from ring_attention_block_amd.hip_events import Event
-    from ring_attention_block_amd.ring import (RingEmulator, ZigzagRing, zigzag_blocks,
-                                               zigzag_plan)
+    from ring_attention_block_amd.ring import (RingEmulator, ZigzagRing, key_split_for, split_keys,
+                                               zigzag_blocks, zigzag_plan)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -555,19 +558,26 @@ def main():
         q = to_dev(blocks[(synth.ROLE_Q, rank)], wl)
         kv = {j: (to_dev(blocks[(synth.ROLE_K, j)], wl), to_dev(blocks[(synth.ROLE_V, j)], wl))
               for j in range(wl.blocks)}
-        states = [_lib.State(1, wl.heads, wl.rows, wl.head_dim, device=dev)]
-        emu = RingEmulator(q.shape, q.dtype, dev, compute_stream=compute)
+        # Without the causal mask a small query block may fold each visiting
+        # block as key ranges into partial states merged at the end.
+        ks = (key_split_for(wl.heads, wl.rows, wl.rows, wl.causal) if args.key_split == "auto"
+              else int(args.key_split))
+        if ks > 1:
+            kv = {j: (split_keys(k, ks), split_keys(v, ks)) for j, (k, v) in kv.items()}
+        states = [_lib.State(ks, wl.heads, wl.rows, wl.head_dim, device=dev)]
+        emu = RingEmulator(kv[0][0].shape, q.dtype, dev, compute_stream=compute)
         cases = [_lib.step_case(rank, j, wl.blocks, wl.causal) for j in range(wl.blocks)]
         flops = ring_flops(wl, rank)
         baseline_q = rank
 
-        fused = not args.unfused
+        fused = not args.unfused or ks > 1
 
         def fold(timers, pool):
             emu.run(states[0], q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
                     step_timers=timers, timer_events=pool,
-                    finalize_out=outs[0] if fused else None)
+                    finalize_out=outs[0] if fused else None, key_split=ks)
     else:
+        ks = 1
         # Zigzag: the sequence in 2P pieces of c/2 tokens; the rank holds
         # pieces (rank, 2P-1-rank), and each visit is up to four piece products.
         step_wl = synth.zigzag_workload(wl)
@@ -596,8 +606,8 @@ def main():
             zz.run(states, qs, source, rank, wl.blocks, wl.causal, wl.scale,
                    step_timers=timers, timer_events=pool, finalize_outs=outs if fused else None)
 
-    outs = [(torch.empty(st.o.shape, dtype=torch.float32, device=dev),
-             torch.empty(st.m.shape, dtype=torch.float32, device=dev)) for st in states]
+    outs = [(torch.empty((1, *st.o.shape[1:]), dtype=torch.float32, device=dev),
+             torch.empty((1, *st.m.shape[1:]), dtype=torch.float32, device=dev)) for st in states]
 
     def one_ring(timers=None, pool=None):
         fold(timers, pool)
@@ -654,7 +664,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
         "config": {"workload": wl.name, "rank": rank, "partition": args.partition,
-                   "fused_init_finalize": fused,
+                   "fused_init_finalize": fused, "key_split": ks,
                    "heads": wl.heads, "head_dim": wl.head_dim, "rows_per_block": wl.rows,
                    "blocks": wl.blocks, "causal": wl.causal, "tokens": wl.tokens,
                    "flop_per_step": flops,

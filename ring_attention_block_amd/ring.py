@@ -24,6 +24,14 @@ Two partitions of the sequence over the P ranks:
     (ZigzagRing).  Each visit is then up to four ra_step calls on sub-block
     pairs; ra_step's causal case test on 2P sub-block indices already gives
     the skip / diagonal / full case of each pair.
+
+Without the causal mask, a ring whose query block is too small to occupy the
+chip can fold each visiting block as key_split ranges of keys into key_split
+partial states, merged once at the end (key_split_for, split_keys,
+RingEmulator.run): the merge of partial online-softmax states ("RingAttention
+... 10M Tokens", the architecture section; "Ring Attention Math Deep",
+online-softmax identity) makes the result independent of how the keys are
+grouped, up to floating-point order.
 """
 from __future__ import annotations
 
@@ -38,6 +46,32 @@ from .hip_events import Event
 def ring_order(rank: int, blocks: int) -> list:
     """Block visited at ring step s: (rank - s) mod blocks."""
     return [(rank - s) % blocks for s in range(blocks)]
+
+
+def key_split_for(batch_heads: int, rows: int, kv_rows: int, causal: bool,
+                  compute_units: int = 256) -> int:
+    """Key ranges per visiting block for RingEmulator.run: 1 under the causal
+    mask (ra_step needs equal blocks there) or when the step's grid of
+    128-row query tiles already covers the compute units; otherwise the
+    smallest of 2, 4 whose grid covers them, as long as each range is a whole
+    number of 64-key tiles."""
+    if causal:
+        return 1
+    tiles = batch_heads * ((rows + 127) // 128)
+    s = 1
+    while s < 4 and tiles * s < compute_units and kv_rows % (2 * s * 64) == 0:
+        s *= 2
+    return s
+
+
+def split_keys(t: torch.Tensor, parts: int) -> torch.Tensor:
+    """[1, H, n, d] -> [parts, H, n / parts, d]: batch entry p holds keys
+    p*n/parts .. (p+1)*n/parts - 1 (the layout RingEmulator.run takes with
+    key_split = parts, and the part order of ra_merge_finalize)."""
+    _, h, n, d = t.shape
+    if t.shape[0] != 1 or n % parts:
+        raise ValueError("split_keys: needs batch 1 and a row count divisible by parts")
+    return t.view(1, h, parts, n // parts, d).permute(0, 2, 1, 3, 4).reshape(parts, h, n // parts, d).contiguous()
 
 
 def zigzag_blocks(rank: int, ranks: int) -> tuple:
@@ -171,7 +205,8 @@ class RingEmulator:
     def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
             rank: int, num_blocks: int, causal: bool, scale: float,
             order: Sequence[int] | None = None, init: bool = True,
-            step_timers: list | None = None, timer_events=None, finalize_out=None) -> list:
+            step_timers: list | None = None, timer_events=None, finalize_out=None,
+            key_split: int = 1) -> list:
         """Contiguous partition: fold the blocks of `order` (default: the ring
         order of `rank`) into st.
 
@@ -185,30 +220,44 @@ class RingEmulator:
         finalize into its first and last launched steps (ra_step_ex): the
         first starts from the empty state (when init), the last writes
         o_out, lse_out as finalize would, instead of the state.
+        key_split > 1 (no causal mask; query batch 1): kv_source(j) returns
+        the blocks in split_keys layout [key_split, H, c / key_split, d], st
+        has batch key_split (one partial state per key range), every step
+        reads the one query block for all of them (RA_STEP_Q_BROADCAST), and
+        finalize_out, if given, is written by one ra_merge_finalize over the
+        key_split partial states after the last step.
         Returns the causal case of each step.
         """
+        if key_split > 1 and (causal or q.shape[0] != 1 or st.shape[0] != key_split):
+            raise ValueError("key_split needs no causal mask, a query batch of 1 and a state batch of key_split")
         order = ring_order(rank, num_blocks) if order is None else list(order)
         all_cases = [_lib.step_case(rank, j, num_blocks, causal) for j in order]
         launched = [s for s, c in enumerate(all_cases) if c != _lib.RA_CASE_SKIP]
         fuse = finalize_out is not None and len(launched) > 0
+        fuse_finalize = fuse and key_split == 1
         if init and not fuse:
             _lib.state_init(st, self.compute)
         cases = []
 
         def fold(s, j, kv):
             case = all_cases[s]
-            flags = 0
+            flags = _lib.RA_STEP_Q_BROADCAST if key_split > 1 else 0
             if fuse and init and s == launched[0]:
                 flags |= _lib.RA_STEP_FRESH
-            if fuse and s == launched[-1]:
+            if fuse_finalize and s == launched[-1]:
                 flags |= _lib.RA_STEP_FINALIZE
             self.step(st, q, kv[0], kv[1], rank, j, num_blocks, causal, scale, case,
-                      step_timers, timer_events, flags, finalize_out if flags else (None, None))
+                      step_timers, timer_events, flags,
+                      finalize_out if flags & _lib.RA_STEP_FINALIZE else (None, None))
             cases.append(case)
 
         self.visit(order, kv_source, fold, busy=lambda s: all_cases[s] != _lib.RA_CASE_SKIP)
-        if finalize_out is not None and not fuse:
-            _lib.finalize(st, stream=self.compute, o_out=finalize_out[0], lse_out=finalize_out[1])
+        if finalize_out is not None:
+            if key_split > 1:
+                _lib.merge_finalize(st, key_split, stream=self.compute, o_out=finalize_out[0],
+                                    lse_out=finalize_out[1])
+            elif not fuse:
+                _lib.finalize(st, stream=self.compute, o_out=finalize_out[0], lse_out=finalize_out[1])
         return cases
 
 

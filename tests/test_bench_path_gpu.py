@@ -24,7 +24,7 @@ torch = pytest.importorskip("torch")
 
 from ring_attention_block_amd import _lib, synth
 from ring_attention_block_amd.hip_events import Event
-from ring_attention_block_amd.ring import RingEmulator, ring_order
+from ring_attention_block_amd.ring import RingEmulator, key_split_for, ring_order, split_keys
 
 from _helpers import assert_close, gen_blocks, oracle_rank, to_device, tol_for
 
@@ -60,23 +60,28 @@ class Inputs:
         self.q = to_device(self.cache[key], self.wl)
 
 
-def bench_ring(inp, rank, causal, order=None, free_hook=None, out_dtype=torch.float32):
+def bench_ring(inp, rank, causal, order=None, free_hook=None, out_dtype=torch.float32,
+               key_split=None):
     """One ring exactly as bench.py enqueues it: own compute stream, fused
     init and finalize, every launched step timed by events bound to its
-    dispatch (drawn from a pool created beforehand)."""
+    dispatch (drawn from a pool created beforehand); without the causal mask
+    a small query block takes bench.py's key split (key_split_for) unless
+    key_split is given."""
     wl = inp.wl
+    ks = key_split_for(wl.heads, wl.rows, wl.rows, causal) if key_split is None else key_split
+    kv = inp.kv if ks == 1 else {j: (split_keys(k, ks), split_keys(v, ks)) for j, (k, v) in inp.kv.items()}
     compute = torch.cuda.Stream()
-    st = _lib.State(1, wl.heads, wl.rows, wl.head_dim)
-    emu = RingEmulator(inp.q.shape, inp.q.dtype, compute_stream=compute)
+    st = _lib.State(ks, wl.heads, wl.rows, wl.head_dim)
+    emu = RingEmulator(kv[next(iter(kv))][0].shape, inp.q.dtype, compute_stream=compute)
     emu.free_hook = free_hook
-    o = torch.empty(st.o.shape, dtype=out_dtype, device="cuda")
-    lse = torch.empty(st.m.shape, dtype=torch.float32, device="cuda")
+    o = torch.empty((1, *st.o.shape[1:]), dtype=out_dtype, device="cuda")
+    lse = torch.empty((1, *st.m.shape[1:]), dtype=torch.float32, device="cuda")
     steps = ring_order(rank, wl.blocks) if order is None else list(order)
     launched = sum(_lib.step_case(rank, j, wl.blocks, causal) != _lib.RA_CASE_SKIP for j in steps)
     pool = iter([Event(timing=True) for _ in range(2 * launched)])
     timers = []
-    emu.run(st, inp.q, lambda j: inp.kv[j], rank, wl.blocks, causal, wl.scale, order=order,
-            step_timers=timers, timer_events=pool, finalize_out=(o, lse))
+    emu.run(st, inp.q, lambda j: kv[j], rank, wl.blocks, causal, wl.scale, order=order,
+            step_timers=timers, timer_events=pool, finalize_out=(o, lse), key_split=ks)
     torch.cuda.synchronize()
     assert len(timers) == launched
     assert all(a.elapsed_time(b) > 0 for _, a, b in timers)
@@ -172,8 +177,16 @@ def test_rescale_stress_every_row_both_orders():
         o, lse = bench_ring(inp, rank, False, order=order)
         check_all(C3, o, lse, want, name)
         res.append((o, lse))
+    # The benchmarked ring folds each block as two key halves (the query block
+    # alone would fill half the chip) and merges them at the end; the plain
+    # ring folds whole blocks.  Both are within the tolerance of the oracle
+    # (above) and of each other; the unsplit ring through the benchmarked path
+    # is bit-identical to the plain one.
+    assert key_split_for(C3.heads, C3.rows, C3.rows, False) == 2
     o2, lse2 = plain_ring(inp, rank, False, order=fwd)
-    assert torch.equal(res[0][0], o2) and torch.equal(res[0][1], lse2)
+    assert float((res[0][0] - o2).abs().max()) <= 2e-2 and float((res[0][1] - lse2).abs().max()) <= 5e-3
+    o1, lse1 = bench_ring(inp, rank, False, order=fwd, key_split=1)
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2)
     assert float((res[0][0] - res[1][0]).abs().max()) <= 2e-2
     assert float((res[0][1] - res[1][1]).abs().max()) <= 5e-3
 
@@ -249,6 +262,47 @@ def test_extreme_scores(case):
         o, lse = fn(inp, rank, causal, order=steps)
         assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), f"{label}: non-finite"
         check_all(wl, o, lse, want, f"{name} {label}", lse_slack=slack)
+
+
+# --------------------------------------------------- key split
+
+# (name, dtype, heads, head_dim, rows, P, rank, spike, spike_blocks, spike_key, key_split, order)
+KSPLIT = [
+    ("bf16_d128_halves", "bf16", 4, 128, 512, 3, 2, 0.0, (), -1, 2, None),
+    ("bf16_d64_quarters", "bf16", 2, 64, 1024, 4, 1, 0.0, (), -1, 4, None),
+    ("bf16_d128_quarters_reversed", "bf16", 3, 128, 1024, 3, 0, 0.0, (), -1, 4, "rev"),
+    ("f32_d64_halves", "f32", 2, 64, 256, 3, 0, 0.0, (), -1, 2, None),
+    ("f32_d128_quarters", "f32", 1, 128, 512, 2, 1, 0.0, (), -1, 4, None),
+    # Score offsets of 10^2 in one visited block, and one key dominating its rows
+    # from the second key half only (one partial state holds the maximum).
+    ("bf16_spike_block", "bf16", 2, 128, 512, 3, 2, 600.0, (1,), -1, 2, None),
+    ("bf16_one_key_second_half", "bf16", 2, 128, 512, 3, 2, 900.0, (0,), 400, 2, "rev"),
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", KSPLIT, ids=[c[0] for c in KSPLIT])
+def test_key_split_ring(case):
+    """Without the causal mask, every visiting block folded as key_split
+    ranges of keys into as many partial states (the query block broadcast to
+    all of them) and merged once after the ring (ra_merge_finalize), as
+    bench.py runs a small query block: every row against the oracle, and
+    within tolerance of the unsplit ring."""
+    name, dtype, heads, d, rows, P, rank, spike, blocks, key, ks, order = case
+    wl = synth.Workload(f"ksplit_{name}", 500 + rows + d + ks, heads, d, rows, P, dtype, False, (rank,),
+                        spike=spike, spike_blocks=blocks, spike_key=key)
+    inp = Inputs(wl, rank)
+    steps = ring_order(rank, P)
+    if order == "rev":
+        steps = steps[::-1]
+    want = oracle_every_head(wl, rank, list(range(P)), False, inp.cache)
+    _say(f"{wl.name}: key split {ks}, order {steps}")
+    o, lse = bench_ring(inp, rank, False, order=steps, key_split=ks)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    check_all(wl, o, lse, want, f"{name} split {ks}", lse_slack=_lse_slack(wl, want[1]))
+    o1, lse1 = bench_ring(inp, rank, False, order=steps, key_split=1)
+    tol_o, tol_l = (2e-2, 5e-3) if dtype == "bf16" else (1e-5, 1e-5 + (_lse_slack(wl, want[1]) or 0.0))
+    assert float((o - o1).abs().max()) <= 2 * tol_o and float((lse - lse1).abs().max()) <= 2 * tol_l
 
 
 # --------------------------------------------------- buffer hazards
