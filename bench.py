@@ -160,6 +160,51 @@ def host_info() -> dict:
             "cpu_model": model, "blas": blas}
 
 
+def capture_ring(one_ring, copy_stream, compute, outs):
+    """One untimed ring captured as a HIP graph on the compute stream (the
+    copy stream forks from it through the ring's first event and is joined
+    back at the end), for the untimed rings of the timed region: one graph
+    launch per ring instead of the host enqueueing every copy, wait and step.
+    The graph is used only if its replay reproduces the eager ring's outputs
+    bit for bit, twice, with an eager ring in between; otherwise (None,
+    reason) and every ring runs eagerly."""
+    import torch
+    from ring_attention_block_amd.hip_events import Event
+
+    join = Event()
+
+    def joined():
+        one_ring()
+        join.record(copy_stream)
+        join.wait(compute)
+
+    try:
+        joined()
+        torch.cuda.synchronize()
+        want = [t.clone() for pair in outs for t in pair]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=compute):
+            joined()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for pair in outs:
+                for t in pair:
+                    t.fill_(float("nan"))
+            torch.cuda.synchronize()
+            with torch.cuda.stream(compute):
+                g.replay()
+            torch.cuda.synchronize()
+            got = [t for pair in outs for t in pair]
+            if not all(torch.equal(a, b) for a, b in zip(got, want)):
+                return None, "off: the replay differed from the eager ring"
+            joined()
+            torch.cuda.synchronize()
+        return g, "untimed rings replay one captured ring"
+    except Exception as e:  # capture unsupported here: every ring runs eagerly
+        torch.cuda.synchronize()
+        return None, f"off: capture failed ({type(e).__name__}: {e})"
+
+
 def timed_rings(args) -> int:
     """Timed rings whose step launches carry timing events (every time_every-th)."""
     return (args.steps + args.time_every - 1) // args.time_every
@@ -511,6 +556,8 @@ def main():
     ap.add_argument("--key-split", default="auto", choices=("auto", "1", "2", "4"),
                     help="key ranges per visiting block (no causal mask only): auto splits when "
                          "the query block alone would leave compute units idle")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="enqueue every untimed ring eagerly instead of replaying a captured one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.time_every < 1:
@@ -571,6 +618,7 @@ def main():
         baseline_q = rank
 
         fused = not args.unfused or ks > 1
+        copy_stream = emu.copy
 
         def fold(timers, pool):
             emu.run(states[0], q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
@@ -594,6 +642,7 @@ def main():
         states = [_lib.State(1, wl.heads, step_wl.rows, wl.head_dim, device=dev)
                   for _ in range(2)]
         zz = ZigzagRing(qs[0].shape, qs[0].dtype, dev, compute_stream=compute)
+        copy_stream = zz.emu.copy
         cases = [c for _, prods in zigzag_plan(rank, wl.blocks, wl.causal) for _, _, c in prods]
         c2 = step_wl.rows
         flops = 4 * wl.head_dim * wl.heads * (cases.count(_lib.RA_CASE_FULL) * c2 * c2 +
@@ -623,9 +672,25 @@ def main():
     for _ in range(args.warmup):
         one_ring()
     torch.cuda.synchronize()
+    graph, graph_note = (capture_ring(one_ring, copy_stream, compute, outs) if args.graph
+                         else (None, "off (--no-graph)"))
+
+    def untimed_ring():
+        if graph is None:
+            one_ring()
+        else:
+            with torch.cuda.stream(compute):
+                graph.replay()
+
+    for _ in range(args.warmup):
+        untimed_ring()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(args.steps):
-        one_ring(*((timers, pool) if r % args.time_every == 0 else ()))
+        if r % args.time_every == 0:
+            one_ring(timers, pool)
+        else:
+            untimed_ring()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -665,6 +730,7 @@ def main():
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
         "config": {"workload": wl.name, "rank": rank, "partition": args.partition,
                    "fused_init_finalize": fused, "key_split": ks,
+                   "graph": graph_note,
                    "heads": wl.heads, "head_dim": wl.head_dim, "rows_per_block": wl.rows,
                    "blocks": wl.blocks, "causal": wl.causal, "tokens": wl.tokens,
                    "flop_per_step": flops,

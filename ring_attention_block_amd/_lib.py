@@ -210,17 +210,9 @@ def _dtype_code(t: torch.Tensor) -> int:
 RA_STEP_FRESH, RA_STEP_FINALIZE, RA_STEP_Q_BROADCAST = 1, 2, 4
 
 
-def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
-         scale: float, stream=None, flags: int = 0, o_out=None, lse_out=None, start=None,
-         stop=None) -> int:
-    """Fold block kv_block into st; returns the causal case (0 skip, 1 diag, 2 full).
-
-    flags (ra_step_ex): RA_STEP_FRESH starts from the empty state without
-    reading st; RA_STEP_FINALIZE writes o_out (fp32 or bf16) and lse_out
-    instead of st, as finalize would.  start, stop (ra_step_timed): timing
-    events (objects with a .handle, or raw hipEvent_t values) that take the
-    begin and end of the step kernel's dispatch.
-    """
+def check_step(st: State, q, k, v, flags: int = 0, o_out=None, lse_out=None) -> None:
+    """The checks step() makes before any library call: operand layouts,
+    dtypes and shapes against the state, the finalize outputs, GPU memory."""
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_input(name, t)
     if not (q.dtype == k.dtype == v.dtype):
@@ -239,15 +231,40 @@ def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causa
             _check_buf("lse_out", lse_out, (b, h, r), _F32)
     _on_gpu(q=q, k=k, v=v, o_out=o_out, lse_out=lse_out)
     _check_state(st)
+
+
+def step(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
+         scale: float, stream=None, flags: int = 0, o_out=None, lse_out=None, start=None,
+         stop=None) -> int:
+    """Fold block kv_block into st; returns the causal case (0 skip, 1 diag, 2 full).
+
+    flags (ra_step_ex): RA_STEP_FRESH starts from the empty state without
+    reading st; RA_STEP_FINALIZE writes o_out (fp32 or bf16) and lse_out
+    instead of st, as finalize would.  start, stop (ra_step_timed): timing
+    events (objects with a .handle, or raw hipEvent_t values) that take the
+    begin and end of the step kernel's dispatch.
+    """
+    check_step(st, q, k, v, flags, o_out, lse_out)
+    return step_checked(st, q, k, v, q_block, kv_block, num_blocks, causal, scale, stream, flags,
+                        o_out, lse_out, start, stop)
+
+
+def step_checked(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
+                 scale: float, stream=None, flags: int = 0, o_out=None, lse_out=None, start=None,
+                 stop=None) -> int:
+    """step() without its Python checks, for a caller that ran check_step()
+    on tensors of exactly these shapes, dtypes and devices (the ring driver:
+    its own receive buffers, and each ring's first block).  The library still
+    makes its own checks (pointers, alignment, overlaps, sizes)."""
     if flags == 0 and start is None and stop is None:
-        _check(lib().ra_step(ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+        _check(lib().ra_step(ctypes.byref(st.c), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
                              k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
                              _stream(stream)))
     else:
         out_code = RA_BF16 if o_out is not None and o_out.dtype == torch.bfloat16 else RA_F32
-        args = (ctypes.byref(st.c), _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), k.shape[2], q_block,
-                kv_block, num_blocks, int(causal), float(scale), int(flags), _ptr(o_out), out_code,
-                _ptr(lse_out))
+        args = (ctypes.byref(st.c), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), k.shape[2],
+                q_block, kv_block, num_blocks, int(causal), float(scale), int(flags), _ptr(o_out),
+                out_code, _ptr(lse_out))
         if start is None and stop is None:
             _check(lib().ra_step_ex(*args, _stream(stream)))
         else:
@@ -313,6 +330,16 @@ def stage_block(dst: torch.Tensor, src: torch.Tensor, stream=None, alone: bool =
         _check(lib().ra_stage_block_ex(_ptr(dst), _ptr(src), n, RA_STAGE_ALONE, _stream(stream)))
     else:
         _check(lib().ra_stage_block(_ptr(dst), _ptr(src), n, _stream(stream)))
+
+
+def stage_block_checked(dst: torch.Tensor, src: torch.Tensor, stream=None, alone: bool = False) -> None:
+    """stage_block() without its Python checks, for a caller that checked
+    both tensors (contiguous GPU tensors of one shape and dtype)."""
+    n = src.numel() * src.element_size()
+    if alone:
+        _check(lib().ra_stage_block_ex(dst.data_ptr(), src.data_ptr(), n, RA_STAGE_ALONE, _stream(stream)))
+    else:
+        _check(lib().ra_stage_block(dst.data_ptr(), src.data_ptr(), n, _stream(stream)))
 
 
 def bwd_prepare(o, dout, delta=None, stream=None, dq=None):

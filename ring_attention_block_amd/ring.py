@@ -151,7 +151,14 @@ class RingEmulator:
                 nxt_buf = free_buf
                 alone = busy is not None and not busy(s)
                 for dst, src in zip(self.bufs[nxt_buf], source(order[s + 1])):
-                    _lib.stage_block(dst, src, copy, alone=alone)
+                    # The receive buffers are the emulator's own; a source of
+                    # their shape and dtype, contiguous on the GPU, needs no
+                    # further Python checks (the library checks the rest).
+                    if (isinstance(src, torch.Tensor) and src.shape == dst.shape and
+                            src.dtype == dst.dtype and src.is_cuda and src.is_contiguous()):
+                        _lib.stage_block_checked(dst, src, copy, alone=alone)
+                    else:
+                        _lib.stage_block(dst, src, copy, alone=alone)
                 self.ev_ready[nxt_buf].record(copy)
             if cur_buf is not None:
                 self.ev_ready[cur_buf].wait(comp)
@@ -194,13 +201,15 @@ class RingEmulator:
         return e0, e1
 
     def step(self, st, q, k, v, i, j, num_blocks, causal, scale, case, step_timers=None,
-             timer_events=None, flags=0, out=(None, None)) -> None:
+             timer_events=None, flags=0, out=(None, None), checked=False) -> None:
         """One ra_step (ra_step_ex with flags) on the compute stream; with
         step_timers (see run), ra_step_timed binds a pair of timing events to
-        the step kernel's dispatch."""
+        the step kernel's dispatch.  checked: the operands passed
+        _lib.check_step already (see run)."""
         e0, e1 = self.timer_pair(case, step_timers, timer_events)
-        _lib.step(st, q, k, v, i, j, num_blocks, causal, scale, self.compute, flags=flags,
-                  o_out=out[0], lse_out=out[1], start=e0, stop=e1)
+        launch = _lib.step_checked if checked else _lib.step
+        launch(st, q, k, v, i, j, num_blocks, causal, scale, self.compute, flags=flags,
+               o_out=out[0], lse_out=out[1], start=e0, stop=e1)
 
     def run(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
             rank: int, num_blocks: int, causal: bool, scale: float,
@@ -238,6 +247,17 @@ class RingEmulator:
         if init and not fuse:
             _lib.state_init(st, self.compute)
         cases = []
+        # Every step passes the state, the query block, the finalize outputs
+        # and either the ring's first block (used where it lies) or one of the
+        # receive buffers (every later block is staged into them): checked
+        # once here, so the steps go to the library without Python checks.
+        all_flags = ((_lib.RA_STEP_Q_BROADCAST if key_split > 1 else 0) |
+                     (_lib.RA_STEP_FINALIZE if fuse_finalize else 0))
+        fin = finalize_out if fuse_finalize else (None, None)
+        first = kv_source(order[0])
+        _lib.check_step(st, q, first[0], first[1], all_flags, *fin)
+        if len(order) > 1:
+            _lib.check_step(st, q, self.bufs[0][0], self.bufs[0][1], all_flags, *fin)
 
         def fold(s, j, kv):
             case = all_cases[s]
@@ -248,7 +268,7 @@ class RingEmulator:
                 flags |= _lib.RA_STEP_FINALIZE
             self.step(st, q, kv[0], kv[1], rank, j, num_blocks, causal, scale, case,
                       step_timers, timer_events, flags,
-                      finalize_out if flags & _lib.RA_STEP_FINALIZE else (None, None))
+                      finalize_out if flags & _lib.RA_STEP_FINALIZE else (None, None), checked=True)
             cases.append(case)
 
         self.visit(order, kv_source, fold, busy=lambda s: all_cases[s] != _lib.RA_CASE_SKIP)
