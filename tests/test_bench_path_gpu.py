@@ -305,6 +305,28 @@ def test_key_split_ring(case):
     assert float((o - o1).abs().max()) <= 2 * tol_o and float((lse - lse1).abs().max()) <= 2 * tol_l
 
 
+def test_key_split_caller_merge_and_rejects():
+    """RingEmulator.run(key_split=2) without finalize_out leaves the two
+    partial states to the caller: merging them with ra_merge_finalize gives
+    the fused ring's outputs bit for bit.  A causal ring, or a state whose
+    batch is not the number of ranges, is rejected before any launch."""
+    wl = synth.Workload("ksplit_caller", 808, 2, 128, 512, 3, "bf16", False, (1,))
+    inp = Inputs(wl, 1)
+    o, lse = bench_ring(inp, 1, False, key_split=2)
+    kv = {j: (split_keys(k, 2), split_keys(v, 2)) for j, (k, v) in inp.kv.items()}
+    st = _lib.State(2, wl.heads, wl.rows, wl.head_dim)
+    emu = RingEmulator(kv[0][0].shape, inp.q.dtype)
+    emu.run(st, inp.q, lambda j: kv[j], 1, wl.blocks, False, wl.scale, key_split=2)
+    o2, lse2 = _lib.merge_finalize(st, 2, torch.float32, emu.compute)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    with pytest.raises(ValueError, match="key_split"):
+        emu.run(st, inp.q, lambda j: kv[j], 1, wl.blocks, True, wl.scale, key_split=2)
+    with pytest.raises(ValueError, match="key_split"):
+        emu.run(_lib.State(1, wl.heads, wl.rows, wl.head_dim), inp.q, lambda j: kv[j], 1, wl.blocks,
+                False, wl.scale, key_split=2)
+
+
 # --------------------------------------------------- buffer hazards
 
 def _poison(tensors, stream):
