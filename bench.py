@@ -565,7 +565,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring of one rank is emulated on a "
-              "single MI355X; runs on more than one GPU are not part of this build.",
+              "single MI355X; the library has no multi-GPU ring (no collectives).",
               file=sys.stderr)
         sys.exit(2)
 
