@@ -268,6 +268,45 @@ typedef enum {
 ra_status ra_stage_block_ex(void *dst, const void *src, size_t bytes, uint32_t flags, hipStream_t stream);
 
 /*
+ * One device-to-device copy carried by ra_step_staged.
+ */
+typedef struct {
+  void *dst;        /* written; 16-byte aligned */
+  const void *src;  /* read; 16-byte aligned */
+  size_t bytes;     /* a multiple of 16, below 2^31; 0: nothing */
+} ra_copy;
+
+#define RA_MAX_STEP_COPIES 2
+
+/*
+ * ra_step_timed that also carries out the staging of the next block (the
+ * receive of the next key/value block into the free buffer while the current
+ * one is folded, "Ring Attention Paper Breakdown ...", section 2) inside the
+ * step's own launch: the step kernel's workgroups copy slices of the
+ * n_copies copies between their key tiles, one 16-byte chunk per thread per
+ * tile, each workgroup a share proportional to its key tiles.  A ring then
+ * needs one stream and no events: the next step is ordered after this one's
+ * copies by the stream, and this step's copies after the previous step's
+ * reads of the buffer they refill.  Arguments as in ra_step_timed, plus:
+ *   copies     n_copies ra_copy entries (0 <= n_copies <= RA_MAX_STEP_COPIES,
+ *              copies may be NULL when n_copies == 0).  Every dst range must be
+ *              disjoint from every other dst and src range, from q, k, v, the
+ *              state and the outputs; a src range must be disjoint from what
+ *              the step writes (the state, or o_out and lse_out).
+ * The copies complete when the call completes on the stream.  They run inside
+ * the step kernel for bf16 inputs; for fp32 inputs, and when the call folds
+ * nothing (a skipped block, kv_rows == 0, an empty state), as full-chip copy
+ * kernels (ra_stage_block_ex with RA_STAGE_ALONE) enqueued after whatever the
+ * step enqueues, outside start and stop.  The fold's results are those of
+ * ra_step_timed.  On an error return nothing is enqueued.
+ */
+ra_status ra_step_staged(ra_state *st, const void *q, const void *k, const void *v,
+                         ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
+                         int32_t num_blocks, int32_t causal, float scale, uint32_t flags,
+                         void *o_out, ra_dtype out_dtype, float *lse_out, const ra_copy *copies,
+                         int32_t n_copies, hipEvent_t start, hipEvent_t stop, hipStream_t stream);
+
+/*
  * Backward, per-row term ("Ring Attention：...", section "Backward 需要让梯度也
  * 沿环传播": gradients of every block interaction, probabilities recomputed
  * from the saved log-sum-exp):  delta[row] = sum_x dout[row][x] * o[row][x],

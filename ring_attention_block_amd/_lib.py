@@ -20,7 +20,8 @@ RA_CASE_SKIP, RA_CASE_DIAG, RA_CASE_FULL = 0, 1, 2
 RA_STAGE_ALONE = 1
 
 # Every symbol include/ra.h declares.
-EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_step_timed", "ra_lse_merge",
+EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_step_timed", "ra_step_staged",
+           "ra_lse_merge",
            "ra_finalize", "ra_merge_finalize", "ra_stage_block", "ra_stage_block_ex", "ra_bwd_prepare", "ra_bwd_step",
            "ra_bwd_step_timed",
            "ra_status_string", "ra_last_error")
@@ -30,6 +31,13 @@ class RaState(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("rows", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
                 ("o", ctypes.c_void_p)]
+
+
+class RaCopy(ctypes.Structure):
+    _fields_ = [("dst", ctypes.c_void_p), ("src", ctypes.c_void_p), ("bytes", ctypes.c_size_t)]
+
+
+RA_MAX_STEP_COPIES = 2
 
 
 class RaError(RuntimeError):
@@ -58,6 +66,9 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_uint32, vp, ctypes.c_int, vp, vp]),
             "ra_step_timed": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32,
                                              f32, ctypes.c_uint32, vp, ctypes.c_int, vp, vp, vp, vp]),
+            "ra_step_staged": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32,
+                                              f32, ctypes.c_uint32, vp, ctypes.c_int, vp,
+                                              ctypes.POINTER(RaCopy), i32, vp, vp, vp]),
             "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
             "ra_merge_finalize": (ctypes.c_int, [sp, i32, vp, ctypes.c_int, vp, vp]),
@@ -269,6 +280,53 @@ def step_checked(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: in
             _check(lib().ra_step_ex(*args, _stream(stream)))
         else:
             _check(lib().ra_step_timed(*args, _event(start), _event(stop), _stream(stream)))
+    return step_case(q_block, kv_block, num_blocks, causal)
+
+
+def check_copies(copies) -> None:
+    """The checks step_staged() makes on its (dst, src) tensor pairs: at most
+    RA_MAX_STEP_COPIES, contiguous GPU tensors, equal byte sizes per pair."""
+    if len(copies) > RA_MAX_STEP_COPIES:
+        raise ValueError(f"at most {RA_MAX_STEP_COPIES} copies per step, got {len(copies)}")
+    for n, (dst, src) in enumerate(copies):
+        _check_input(f"copy {n} dst", dst)
+        _check_input(f"copy {n} src", src)
+        _on_gpu(dst=dst, src=src)
+        if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+            raise ValueError(f"copy {n}: sizes differ")
+
+
+def _copy_array(copies):
+    arr = (RaCopy * max(1, len(copies)))()
+    for n, (dst, src) in enumerate(copies):
+        arr[n].dst, arr[n].src = dst.data_ptr(), src.data_ptr()
+        arr[n].bytes = src.numel() * src.element_size()
+    return arr
+
+
+def step_staged(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
+                scale: float, copies=(), stream=None, flags: int = 0, o_out=None, lse_out=None,
+                start=None, stop=None) -> int:
+    """step() that also copies each (dst, src) of `copies` inside the step's
+    launch (ra_step_staged: the next block's staging carried by the fold of
+    the current one).  Returns the causal case."""
+    check_step(st, q, k, v, flags, o_out, lse_out)
+    check_copies(copies)
+    return step_staged_checked(st, q, k, v, q_block, kv_block, num_blocks, causal, scale, copies,
+                               stream, flags, o_out, lse_out, start, stop)
+
+
+def step_staged_checked(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int,
+                        causal: bool, scale: float, copies=(), stream=None, flags: int = 0,
+                        o_out=None, lse_out=None, start=None, stop=None) -> int:
+    """step_staged() without its Python checks, for a caller that ran
+    check_step() and check_copies() on tensors of exactly these shapes, dtypes
+    and devices.  The library still makes its own checks."""
+    out_code = RA_BF16 if o_out is not None and o_out.dtype == torch.bfloat16 else RA_F32
+    _check(lib().ra_step_staged(ctypes.byref(st.c), q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
+                                int(flags), _ptr(o_out), out_code, _ptr(lse_out), _copy_array(copies),
+                                len(copies), _event(start), _event(stop), _stream(stream)))
     return step_case(q_block, kv_block, num_blocks, causal)
 
 

@@ -156,11 +156,67 @@ ra_status ra_state_init(ra_state *st, hipStream_t stream) {
 namespace {
 
 // ra_step and ra_step_ex: every check before anything is enqueued.
+static_assert(RA_MAX_STEP_COPIES == ra::kMaxStepCopies, "one copy limit for the ABI and the kernel");
+
+// The copies a staged step carries: each one's own rules, then every
+// destination disjoint from every other range the call touches and every
+// source disjoint from what the call writes (`writes`), and the launch's work
+// units countable in 31 bits (the kernel cuts the copies by them).
+ra_status check_copies(const char *name, const ra_copy *copies, int32_t n_copies,
+                       const Span *writes, int nw, const Span *reads, int nr, int64_t units_bound) {
+  if (n_copies < 0 || n_copies > RA_MAX_STEP_COPIES)
+    return fail(RA_ERR_INVALID_ARG, "%s: n_copies=%d (0 to %d)", name, n_copies, RA_MAX_STEP_COPIES);
+  if (n_copies > 0 && !copies) return fail(RA_ERR_INVALID_ARG, "%s: NULL copies", name);
+  for (int32_t i = 0; i < n_copies; ++i) {
+    const ra_copy &c = copies[i];
+    if (c.bytes == 0) continue;
+    if (!c.dst || !c.src) return fail(RA_ERR_INVALID_ARG, "%s: copy %d has a NULL pointer", name, i);
+    if (!aligned16(c.dst) || !aligned16(c.src) || c.bytes % 16 != 0)
+      return fail(RA_ERR_INVALID_ARG, "%s: copy %d: pointers must be 16-byte aligned and bytes a multiple of 16",
+                  name, i);
+    if (c.bytes >= ((size_t)1 << 31))
+      return fail(RA_ERR_INVALID_ARG, "%s: copy %d: %zu bytes (below 2^31 per copy)", name, i, c.bytes);
+    if (units_bound >= ((int64_t)1 << 31))
+      return fail(RA_ERR_UNSUPPORTED, "%s: the step is too large to carry copies", name);
+    const Span d{c.dst, (int64_t)c.bytes, "a copy destination"};
+    for (int32_t j = 0; j < n_copies; ++j) {
+      if (copies[j].bytes == 0) continue;
+      const Span sj{copies[j].src, (int64_t)copies[j].bytes, "a copy source"};
+      const Span dj{copies[j].dst, (int64_t)copies[j].bytes, "another copy destination"};
+      if (overlap(d, sj) || (j != i && overlap(d, dj)))
+        return fail(RA_ERR_INVALID_ARG, "%s: copy %d's destination overlaps %s", name, i,
+                    overlap(d, sj) ? sj.name : dj.name);
+    }
+    const Span src{c.src, (int64_t)c.bytes, "a copy source"};
+    for (int j = 0; j < nw; ++j)
+      if (overlap(d, writes[j]) || overlap(src, writes[j]))
+        return fail(RA_ERR_INVALID_ARG, "%s: copy %d overlaps %s", name, i, writes[j].name);
+    for (int j = 0; j < nr; ++j)
+      if (overlap(d, reads[j]))
+        return fail(RA_ERR_INVALID_ARG, "%s: copy %d's destination overlaps %s", name, i, reads[j].name);
+  }
+  return RA_OK;
+}
+
+// Enqueue the copies as full-chip copy kernels (a step that folds nothing, or
+// an fp32 step).
+ra_status launch_copies_alone(const char *name, const ra_copy *copies, int32_t n_copies,
+                              hipStream_t stream) {
+  for (int32_t i = 0; i < n_copies; ++i) {
+    if (copies[i].bytes == 0) continue;
+    (void)hipGetLastError();
+    const ra_status s = hip_status(ra::launch_stage_copy(copies[i].dst, copies[i].src, copies[i].bytes,
+                                                         true, stream), name);
+    if (s != RA_OK) return s;
+  }
+  return ok();
+}
+
 ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k, const void *v,
                     ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
                     int32_t num_blocks, int32_t causal, float scale, uint32_t flags, void *o_out,
                     ra_dtype out_dtype, float *lse_out, hipEvent_t start, hipEvent_t stop,
-                    hipStream_t stream) {
+                    hipStream_t stream, const ra_copy *copies = nullptr, int32_t n_copies = 0) {
   int64_t n = 0;
   ra_status s = check_state(st, name, &n);
   if (s != RA_OK) return s;
@@ -201,14 +257,26 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
     const Span in[] = {{q, q_rows * d * es, "q"}, {k, kv_n * d * es, "k"}, {v, kv_n * d * es, "v"}};
     const Span state[] = {{st->m, n * 4, "state m"}, {st->l, n * 4, "state l"},
                           {st->o, n * d * 4, "state o"}};
+    const Span out[] = {{o_out, n * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"},
+                        {lse_out, n * 4, "lse_out"}};
     if (flags & RA_STEP_FINALIZE) {
-      const Span out[] = {{o_out, n * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"},
-                          {lse_out, n * 4, "lse_out"}};
       const Span rd[] = {in[0], in[1], in[2], state[0], state[1], state[2]};
       s = check_disjoint(name, out, rd);
     } else {
       s = check_disjoint(name, state, in);
     }
+    if (s != RA_OK) return s;
+    if (n_copies != 0) {
+      const bool fin = (flags & RA_STEP_FINALIZE) != 0;
+      const Span w[] = {state[0], state[1], state[2], fin ? out[0] : Span{nullptr, 0, ""},
+                        fin ? out[1] : Span{nullptr, 0, ""}};
+      const int64_t units = (int64_t)st->batch * st->heads * ((st->rows + 127) / 128) *
+                            ((kv_rows + 63) / 64);
+      s = check_copies(name, copies, n_copies, w, 5, in, 3, units);
+      if (s != RA_OK) return s;
+    }
+  } else if (n_copies != 0) {
+    s = check_copies(name, copies, n_copies, nullptr, 0, nullptr, 0, 0);
     if (s != RA_OK) return s;
   }
   if (n == 0 || c == RA_CASE_SKIP || kv_rows == 0) {
@@ -232,10 +300,10 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
       const hipError_t e = hipEventRecord(stop, stream);
       if (e != hipSuccess) return hip_status(e, name);
     }
-    return ok();
+    return launch_copies_alone(name, copies, n_copies, stream);
   }
 
-  ra::StepArgs a;
+  ra::StepArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -252,11 +320,22 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   a.lse_out = (flags & RA_STEP_FINALIZE) ? lse_out : nullptr;
   a.out_bf16 = out_dtype == RA_BF16;
   const ra::StepCase sc = c == RA_CASE_DIAG ? ra::StepCase::Diag : ra::StepCase::Full;
+  if (in_dtype == RA_BF16) {
+    for (int32_t i = 0; i < n_copies; ++i) {
+      if (copies[i].bytes == 0) continue;
+      const int c = a.cp.n++;
+      a.cp.src[c] = copies[i].src;
+      a.cp.dst[c] = copies[i].dst;
+      a.cp.chunks[c] = (uint32_t)(copies[i].bytes / 16);
+    }
+  }
   (void)hipGetLastError();
   const ra::LaunchTiming t{start, stop};
   const hipError_t e = in_dtype == RA_BF16 ? ra::launch_step_bf16(a, st->head_dim, sc, stream, t)
                                            : ra::launch_step_f32(a, st->head_dim, sc, stream, t);
-  return hip_status(e, name);
+  const ra_status r = hip_status(e, name);
+  if (r != RA_OK || in_dtype == RA_BF16) return r;
+  return launch_copies_alone(name, copies, n_copies, stream);
 }
 
 }  // namespace
@@ -283,6 +362,19 @@ ra_status ra_step_timed(ra_state *st, const void *q, const void *k, const void *
                         hipEvent_t stop, hipStream_t stream) {
   return step_impl("ra_step_timed", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks,
                    causal, scale, flags, o_out, out_dtype, lse_out, start, stop, stream);
+}
+
+ra_status ra_step_staged(ra_state *st, const void *q, const void *k, const void *v,
+                         ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
+                         int32_t num_blocks, int32_t causal, float scale, uint32_t flags,
+                         void *o_out, ra_dtype out_dtype, float *lse_out, const ra_copy *copies,
+                         int32_t n_copies, hipEvent_t start, hipEvent_t stop, hipStream_t stream) {
+  if (n_copies < 0 || n_copies > RA_MAX_STEP_COPIES)
+    return fail(RA_ERR_INVALID_ARG, "ra_step_staged: n_copies=%d (0 to %d)", n_copies, RA_MAX_STEP_COPIES);
+  if (n_copies > 0 && !copies) return fail(RA_ERR_INVALID_ARG, "ra_step_staged: NULL copies");
+  return step_impl("ra_step_staged", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks,
+                   causal, scale, flags, o_out, out_dtype, lse_out, start, stop, stream, copies,
+                   n_copies);
 }
 
 ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream) {

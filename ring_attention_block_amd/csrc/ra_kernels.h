@@ -9,6 +9,21 @@
 
 namespace ra {
 
+// Copies a bf16 step launch carries out beside its fold (a ring's next key and
+// value blocks, staged while the current one is folded).  The launch's work is
+// counted in units of one key tile of one workgroup; copy k is cut into
+// consecutive slices of per_unit[k] 16-byte chunks per unit, and each
+// workgroup copies the slices of its own units, one chunk per thread and copy
+// between two of its key tiles (and whatever is left after its last tile).
+constexpr int kMaxStepCopies = 2;
+struct StepCopies {
+  const void *src[kMaxStepCopies];
+  void *dst[kMaxStepCopies];
+  uint32_t chunks[kMaxStepCopies];     // 16-byte chunks of each copy
+  uint32_t per_unit[kMaxStepCopies];   // set by the launcher from its grid
+  int32_t n;                           // copies (0: none)
+};
+
 // Arguments of one ring-step kernel launch.  Tensors are [bh, rows, D].
 struct StepArgs {
   const void *q, *k, *v;  // bf16 (uint16 storage) or fp32, per launcher
@@ -22,6 +37,7 @@ struct StepArgs {
   void *o_out;            // kStepFinalize: O / l ([bh, rows, D], fp32 or bf16), may be NULL
   float *lse_out;         // kStepFinalize: m + ln l ([bh, rows]), may be NULL
   int32_t out_bf16;       // kStepFinalize: o_out is bf16
+  StepCopies cp;          // bf16 launches only (the fp32 launcher ignores it)
 };
 
 // The state is not read: the step starts from the empty state (m = -inf,

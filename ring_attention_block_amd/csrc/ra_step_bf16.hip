@@ -46,6 +46,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ra_kernels.h"
@@ -57,6 +58,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -243,8 +245,10 @@ __device__ __forceinline__ void tile_exp(const f32x16 (&s)[2], RowState &rs, bf1
 
 // kMask: some tile may need the element mask (diagonal block, or a block
 // length that is not a multiple of 64).  kIdle: the query rows are not a
-// multiple of the workgroup's, so some wavefronts may have no rows.
-template <int D, bool kDiag, int kW, bool kMask, bool kIdle>
+// multiple of the workgroup's, so some wavefronts may have no rows.  kCopy:
+// the launch carries copies (StepCopies); without them the copy code compiles
+// away and the kernel keeps its registers for the fold.
+template <int D, bool kDiag, int kW, bool kMask, bool kIdle, bool kCopy>
 __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using T = Tile<D>;
@@ -324,6 +328,68 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   const int kv_end = kDiag ? min(kv_rows, qt * kBM + kBM) : kv_rows;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
   // Tile n uses K and V buffer n % 2.
+
+  // Carried copies (StepCopies): this workgroup's units are [u0, u0 + n_tiles)
+  // in (batch-head, query tile) order; on the diagonal, query tile t holds
+  // (t + 1) kBM / kBN key tiles (all but the last tile of the block are whole).
+  // Each copy's slice is addressed through buffer resources based at its start
+  // and bounded to its length, so lanes past its end load zeros and their
+  // stores are dropped; both copies advance together, one 16-byte chunk per
+  // thread and copy per tick.  A tick (one at the end of each key tile's
+  // iteration) stores the chunks the previous tick loaded and loads the next
+  // ones.  The state is uniform and set up once, so no kernel argument stays
+  // live.  (Non-temporal accesses measured no better: 0.452 against 0.425 ms
+  // for a 16-step ring of 8 heads x 2048 rows.)
+  const uint32_t u0 = kDiag ? (uint32_t)bh * (uint32_t)((kBM / kBN) * (n_qt - 1) * n_qt / 2 +
+                                                         (min(kv_rows, n_qt * kBM) + kBN - 1) / kBN) +
+                                  (uint32_t)((kBM / kBN) * qt * (qt + 1) / 2)
+                            : ((uint32_t)bh * (uint32_t)n_qt + (uint32_t)qt) * (uint32_t)n_tiles;
+  constexpr int kCopyPolicy = 0;   // buffer access cache policy: default
+  __amdgpu_buffer_rsrc_t cp_s0 = make_rsrc(nullptr, 0), cp_d0 = cp_s0, cp_s1 = cp_s0, cp_d1 = cp_s0;
+  // cp_off starts past every slice (slices are below 2^31 bytes), so the first
+  // tick's stores are out of range.
+  uint32_t cp_ticks = 0, cp_t = 0, cp_off = 0x80000000u;
+  u32x4 cp_v0 = {0u, 0u, 0u, 0u}, cp_v1 = cp_v0;
+  if constexpr (kCopy) {
+    uint32_t len_max = 0;
+    auto slice = [&](uint64_t c, uint64_t pu, const void *src, void *dst, __amdgpu_buffer_rsrc_t &rs,
+                     __amdgpu_buffer_rsrc_t &rd) {
+      const uint64_t lo = min((uint64_t)u0 * pu, c), hi = min((uint64_t)(u0 + n_tiles) * pu, c);
+      const uint32_t len = (uint32_t)(hi - lo);
+      rs = make_rsrc(static_cast<const char *>(src) + lo * 16, len * 16u);
+      rd = make_rsrc(static_cast<char *>(dst) + lo * 16, len * 16u);
+      len_max = max(len_max, len);
+    };
+    slice(a.cp.chunks[0], a.cp.per_unit[0], a.cp.src[0], a.cp.dst[0], cp_s0, cp_d0);
+    if (a.cp.n > 1) slice(a.cp.chunks[1], a.cp.per_unit[1], a.cp.src[1], a.cp.dst[1], cp_s1, cp_d1);
+    cp_ticks = (len_max + 64u * kW - 1) / (64u * kW);
+  }
+  // The end of an iteration: the copy tick, then the wait for this
+  // wavefront's tile copies (and its LDS accesses) before the barrier.  While
+  // the slices last (one uniform test), the tick stores both slots' previous
+  // chunks and loads both next ones without further branches: accesses that
+  // fall outside a slice (before the first load, past the last chunk, a second
+  // copy that does not exist) are out of range, so they load zeros and store
+  // nothing.  Its four accesses are the last vector memory accesses issued,
+  // and those complete in issue order, so vmcnt(4) leaves exactly them in
+  // flight: no tile waits for a copy's memory latency.  Once the slices are
+  // done the iteration ends as without copies (issuing the out-of-range
+  // accesses in every iteration cost 2% of the step).
+  auto close = [&]() {
+    if constexpr (kCopy) {
+      if (cp_t <= cp_ticks) {
+        __builtin_amdgcn_raw_buffer_store_b128(cp_v0, cp_d0, cp_off, 0, kCopyPolicy);
+        __builtin_amdgcn_raw_buffer_store_b128(cp_v1, cp_d1, cp_off, 0, kCopyPolicy);
+        cp_off = (cp_t * 64u * kW + (uint32_t)tid) * 16u;
+        cp_v0 = __builtin_amdgcn_raw_buffer_load_b128(cp_s0, cp_off, 0, kCopyPolicy);
+        cp_v1 = __builtin_amdgcn_raw_buffer_load_b128(cp_s1, cp_off, 0, kCopyPolicy);
+        ++cp_t;
+        __builtin_amdgcn_s_waitcnt(4 | (7 << 4));   // vmcnt(4) lgkmcnt(0)
+        return;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  };
 
   // A ragged last tile that is the first use of its LDS buffers must not see
   // uninitialised LDS past the block end: zero those rows.  A later use of a
@@ -538,7 +604,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) s_cur[sb] = s_nxt[sb];
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of K(t+2), V(t+1) landed
+    close();   // this wavefront's copies of K(t+2), V(t+1) landed
     __syncthreads();
   };
 
@@ -664,25 +730,46 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       a.lse_out[(size_t)bh * rows + row] = lr > 0.f ? m_nat + logf(lr) : -INFINITY;
     }
   }
+  // The rest of this workgroup's slices of the carried copies (a workgroup
+  // with fewer key tiles than its slices need iterations).
+  if constexpr (kCopy) {
+    while (cp_t <= cp_ticks) close();
+    __builtin_amdgcn_raw_buffer_store_b128(cp_v0, cp_d0, cp_off, 0, kCopyPolicy);
+    __builtin_amdgcn_raw_buffer_store_b128(cp_v1, cp_d1, cp_off, 0, kCopyPolicy);
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 template <int D, bool kDiag, int kW>
-hipError_t launch(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
+hipError_t launch(StepArgs a, hipStream_t s, const LaunchTiming &t) {
   constexpr int kBM = 32 * kW;
   const int n_qt = (a.rows + kBM - 1) / kBM;
   const dim3 grid((unsigned)((int64_t)a.bh * n_qt)), block(64 * kW);
-  auto go = [&](void (*kernel)(StepArgs)) {
-    return launch_one(kernel, grid, block, s, t.start, t.stop, a);
+  if (a.cp.n > 0) {
+    // Units of the launch (key tiles summed over its workgroups), counted as
+    // the kernel counts each workgroup's (u0 and n_tiles there).
+    const int64_t per = kBM / kBN;
+    const int64_t units =
+        kDiag ? (int64_t)a.bh * (per * (n_qt - 1) * n_qt / 2 +
+                                 (std::min<int64_t>(a.kv_rows, (int64_t)n_qt * kBM) + kBN - 1) / kBN)
+              : (int64_t)a.bh * n_qt * ((a.kv_rows + kBN - 1) / kBN);
+    for (int k = 0; k < a.cp.n; ++k)
+      a.cp.per_unit[k] = (uint32_t)(((int64_t)a.cp.chunks[k] + units - 1) / units);
+  }
+  auto go = [&](void (*plain)(StepArgs), void (*copying)(StepArgs)) {
+    return launch_one(a.cp.n > 0 ? copying : plain, grid, block, s, t.start, t.stop, a);
   };
-  if constexpr (kDiag) return go(step_bf16_kernel<D, true, kW, true, false>);
+  if constexpr (kDiag)
+    return go(step_bf16_kernel<D, true, kW, true, false, false>, step_bf16_kernel<D, true, kW, true, false, true>);
   const bool mask = a.kv_rows % kBN != 0, idle = a.rows % kBM != 0;
   if (mask) {
-    return idle ? go(step_bf16_kernel<D, false, kW, true, true>)
-                : go(step_bf16_kernel<D, false, kW, true, false>);
+    return idle ? go(step_bf16_kernel<D, false, kW, true, true, false>, step_bf16_kernel<D, false, kW, true, true, true>)
+                : go(step_bf16_kernel<D, false, kW, true, false, false>,
+                     step_bf16_kernel<D, false, kW, true, false, true>);
   }
-  return idle ? go(step_bf16_kernel<D, false, kW, false, true>)
-              : go(step_bf16_kernel<D, false, kW, false, false>);
+  return idle ? go(step_bf16_kernel<D, false, kW, false, true, false>, step_bf16_kernel<D, false, kW, false, true, true>)
+              : go(step_bf16_kernel<D, false, kW, false, false, false>,
+                   step_bf16_kernel<D, false, kW, false, false, true>);
 }
 
 // Full blocks: 8-wavefront workgroups (256 query rows share each key/value

@@ -64,6 +64,21 @@ def key_split_for(batch_heads: int, rows: int, kv_rows: int, causal: bool,
     return s
 
 
+def staging_for(batch_heads: int, rows: int, kv_rows: int, head_dim: int, skipped_visits: int,
+                min_step_gflop: float = 100.0) -> str:
+    """Staging mode of a forward ring (RingEmulator's `staging`): "side" when
+    every visit launches a step of at least min_step_gflop of matrix work
+    (4 * head_dim * batch_heads * rows * kv_rows FLOP): there a copy kernel
+    beside the step hides almost entirely and the cross-stream events cost
+    little against the step; otherwise "fused" (short steps, where the events
+    and the separate copy launches dominate, and visits with nothing to fold,
+    whose copies then run alone on the compute stream without events)."""
+    step_flop = 4.0 * head_dim * batch_heads * rows * kv_rows
+    if skipped_visits == 0 and step_flop >= min_step_gflop * 1e9:
+        return "side"
+    return "fused"
+
+
 def split_keys(t: torch.Tensor, parts: int) -> torch.Tensor:
     """[1, H, n, d] -> [parts, H, n / parts, d]: batch entry p holds keys
     p*n/parts .. (p+1)*n/parts - 1 (the layout RingEmulator.run takes with
@@ -101,11 +116,23 @@ class RingEmulator:
     tensors_per_visit: tensors staged per visiting rank (K, V for the
     contiguous partition; K and V of two sub-blocks for zigzag);
     extra_specs: (shape, dtype) of further tensors staged with them (the
-    travelling dK, dV accumulators of the backward).
+    travelling dK, dV accumulators of the backward);
+    staging: "side" (copy kernels on a side stream, events between the
+    streams) or "fused" (the copies ride in the step launches, ra_step_staged;
+    forward rings only).
     """
 
     def __init__(self, shape, dtype, device="cuda", compute_stream=None, copy_stream=None,
-                 tensors_per_visit: int = 2, extra_specs=()):
+                 tensors_per_visit: int = 2, extra_specs=(), staging: str = "side"):
+        if staging not in ("side", "fused"):
+            raise ValueError(f"staging must be 'side' or 'fused', got {staging!r}")
+        # staging "side": each block is staged by a copy kernel on the copy
+        # stream, ordered against the steps by events.  "fused": the copies of
+        # the next visit ride in the current visit's step launches
+        # (ra_step_staged), on the compute stream alone, with no events.
+        self.staging = staging
+        self.pending = []            # fused: (dst, src) copies not yet given to a launch
+        self.copies_per_launch = 2   # fused: copies one step launch takes at most
         self.shape = tuple(shape)
         self.dtype = dtype
         specs = [(self.shape, dtype)] * tensors_per_visit + [(tuple(sh), dt) for sh, dt in extra_specs]
@@ -137,6 +164,9 @@ class RingEmulator:
         busy(s), if given, says whether step s launches any compute; the
         staging that overlaps a step that does not (a skipped causal block)
         runs alone and takes the whole chip (ra_stage_block_ex)."""
+        if self.staging == "fused":
+            self._visit_fused(order, source, fold, drain, busy)
+            return
         comp, copy = self.compute, self.copy
         # Copies of this run start after everything already queued on the
         # compute stream (earlier runs may still read the buffers).
@@ -186,6 +216,53 @@ class RingEmulator:
             self.ev_start.record(copy)
             self.ev_start.wait(comp)
 
+    def _visit_fused(self, order, source, fold, drain, busy) -> None:
+        """visit() with the staging carried by the step launches: the copies
+        of order[s+1] into the free buffer are handed to the launches of step
+        s (see step), all on the compute stream; the stream orders each copy
+        after the reads of the buffer it refills and before the step that
+        reads it.  Copies no launch took (a skipped block) run alone after the
+        step's launches."""
+        if drain is not None:
+            raise ValueError("fused staging carries no drain: a backward ring stages on the side stream")
+        comp = self.compute
+        cur = source(order[0])
+        cur_buf = None
+        free_buf = 0
+        for s, j in enumerate(order):
+            nxt_buf = None
+            self.pending = []
+            if s + 1 < len(order):
+                nxt_buf = free_buf
+                self.pending = list(zip(self.bufs[nxt_buf], source(order[s + 1])))
+            self.last_stop = None
+            fold(s, j, cur)
+            for dst, src in self.pending:
+                if (isinstance(src, torch.Tensor) and src.shape == dst.shape and
+                        src.dtype == dst.dtype and src.is_cuda and src.is_contiguous()):
+                    _lib.stage_block_checked(dst, src, comp, alone=True)
+                else:
+                    _lib.stage_block(dst, src, comp, alone=True)
+            self.pending = []
+            if cur_buf is not None and self.free_hook is not None:
+                self.free_hook(cur, comp)
+            if nxt_buf is not None:
+                free_buf = cur_buf if cur_buf is not None else 1 - nxt_buf
+                cur, cur_buf = self.bufs[nxt_buf], nxt_buf
+
+    def _take_copies(self, case) -> list:
+        """The copies a launched step carries (fused staging): up to
+        copies_per_launch of the pending ones."""
+        if self.staging != "fused" or case == _lib.RA_CASE_SKIP or not self.pending:
+            return []
+        take = self.pending[:self.copies_per_launch]
+        self.pending = self.pending[self.copies_per_launch:]
+        for dst, src in take:
+            if not (isinstance(src, torch.Tensor) and src.shape == dst.shape and src.dtype == dst.dtype
+                    and src.is_cuda and src.is_contiguous()):
+                _lib.check_copies([(dst, src)])
+        return take
+
     def timer_pair(self, case, step_timers, timer_events):
         """(start, stop) timing events for a launch that step_timers records,
         or (None, None).  The stop event also marks the end of the visit's
@@ -207,6 +284,12 @@ class RingEmulator:
         the step kernel's dispatch.  checked: the operands passed
         _lib.check_step already (see run)."""
         e0, e1 = self.timer_pair(case, step_timers, timer_events)
+        copies = self._take_copies(case)
+        if copies:
+            launch = _lib.step_staged_checked if checked else _lib.step_staged
+            launch(st, q, k, v, i, j, num_blocks, causal, scale, copies, self.compute, flags=flags,
+                   o_out=out[0], lse_out=out[1], start=e0, stop=e1)
+            return
         launch = _lib.step_checked if checked else _lib.step
         launch(st, q, k, v, i, j, num_blocks, causal, scale, self.compute, flags=flags,
                o_out=out[0], lse_out=out[1], start=e0, stop=e1)
@@ -322,11 +405,12 @@ class ZigzagRing:
     """
 
     def __init__(self, sub_shape, dtype, device="cuda", compute_stream=None, copy_stream=None,
-                 backward: bool = False):
+                 backward: bool = False, staging: str = "side"):
         # backward: also stage the fp32 dK, dV of the visiting rank's two sub-blocks.
+        # staging: as for RingEmulator ("fused": forward rings only).
         extra = [(tuple(sub_shape), torch.float32)] * 4 if backward else ()
         self.emu = RingEmulator(sub_shape, dtype, device, compute_stream, copy_stream,
-                                tensors_per_visit=4, extra_specs=extra)
+                                tensors_per_visit=4, extra_specs=extra, staging=staging)
         self.backward = backward
 
     @property

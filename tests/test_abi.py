@@ -337,3 +337,40 @@ def test_bwd_rejects_overlapping_gradients_and_inputs(L):
     assert prep(delta=A(3) + 512) == _lib.RA_ERR_INVALID_ARG             # delta inside dq
     assert prep(delta=A(0)) == _lib.RA_ERR_INVALID_ARG                   # delta on o
     assert b"overlap" in L.ra_last_error()
+
+
+def _staged(L, st, copies, n=None, q=A(3), k=A(4), v=A(5), flags=0, o_out=None, lse_out=None,
+            i=1, j=0, causal=1):
+    arr = (_lib.RaCopy * max(1, len(copies)))(*[_lib.RaCopy(d, s, b) for d, s, b in copies])
+    n = len(copies) if n is None else n
+    return L.ra_step_staged(ctypes.byref(st), q, k, v, _lib.RA_BF16, st.rows, i, j, 2, causal, 0.125,
+                            flags, o_out, _lib.RA_F32, lse_out, arr if copies or n else None, n,
+                            None, None, None)
+
+
+def test_step_staged_rejects_before_enqueue(L):
+    st = _state()
+    big = 1 << 20
+    ok_copy = (A(8), A(9), big)
+    bad = _lib.RA_ERR_INVALID_ARG
+    assert _staged(L, st, [ok_copy] * 3) == bad                       # more than RA_MAX_STEP_COPIES
+    assert _staged(L, st, [], n=-1) == bad
+    assert L.ra_step_staged(ctypes.byref(st), A(3), A(4), A(5), 1, 128, 1, 0, 2, 1, 0.125, 0, None, 0,
+                            None, None, 1, None, None, None) == bad   # NULL copies
+    assert _staged(L, st, [(0, A(9), big)]) == bad                    # NULL dst
+    assert _staged(L, st, [(A(8) + 8, A(9), big)]) == bad             # misaligned
+    assert _staged(L, st, [(A(8), A(9), big + 8)]) == bad             # not a multiple of 16
+    assert b"16" in L.ra_last_error()
+    assert _staged(L, st, [(A(8), A(9), 1 << 31)]) == bad             # 2^31 bytes
+    assert _staged(L, st, [(A(8), A(8) + 4096, big)]) == bad          # dst overlaps its src
+    assert b"overlap" in L.ra_last_error()
+    assert _staged(L, st, [ok_copy, (A(8) + 64, A(10), 4096)]) == bad  # two destinations overlap
+    assert _staged(L, st, [ok_copy, (A(10), A(8), 4096)]) == bad       # dst is another copy's src
+    assert _staged(L, st, [(A(4), A(9), 4096)]) == bad                # dst over k
+    assert _staged(L, st, [(A(3) + 4096, A(9), 4096)]) == bad         # dst over q
+    assert _staged(L, st, [(A(2), A(9), 4096)]) == bad                # dst over the state
+    assert _staged(L, st, [(A(8), A(2), 4096)]) == bad                # src over the state (written)
+    assert _staged(L, st, [(A(8), A(6), 4096)], flags=_lib.RA_STEP_FINALIZE, o_out=A(6)) == bad
+    assert b"o_out" in L.ra_last_error()
+    # the step's own checks still apply
+    assert _staged(L, st, [ok_copy], q=A(3) + 8) == bad

@@ -24,7 +24,7 @@ torch = pytest.importorskip("torch")
 
 from ring_attention_block_amd import _lib, synth
 from ring_attention_block_amd.hip_events import Event
-from ring_attention_block_amd.ring import RingEmulator, key_split_for, ring_order, split_keys
+from ring_attention_block_amd.ring import RingEmulator, key_split_for, ring_order, split_keys, staging_for
 
 from _helpers import assert_close, gen_blocks, oracle_rank, to_device, tol_for
 
@@ -61,23 +61,28 @@ class Inputs:
 
 
 def bench_ring(inp, rank, causal, order=None, free_hook=None, out_dtype=torch.float32,
-               key_split=None):
+               key_split=None, staging=None):
     """One ring exactly as bench.py enqueues it: own compute stream, fused
     init and finalize, every launched step timed by events bound to its
     dispatch (drawn from a pool created beforehand); without the causal mask
     a small query block takes bench.py's key split (key_split_for) unless
-    key_split is given."""
+    key_split is given, and the staging mode is bench.py's (staging_for)
+    unless staging is given."""
     wl = inp.wl
     ks = key_split_for(wl.heads, wl.rows, wl.rows, causal) if key_split is None else key_split
     kv = inp.kv if ks == 1 else {j: (split_keys(k, ks), split_keys(v, ks)) for j, (k, v) in inp.kv.items()}
+    steps = ring_order(rank, wl.blocks) if order is None else list(order)
+    step_cases = [_lib.step_case(rank, j, wl.blocks, causal) for j in steps]
+    launched = sum(c != _lib.RA_CASE_SKIP for c in step_cases)
+    if staging is None:
+        staging = staging_for(ks * wl.heads, wl.rows, wl.rows // ks, wl.head_dim,
+                              step_cases.count(_lib.RA_CASE_SKIP))
     compute = torch.cuda.Stream()
     st = _lib.State(ks, wl.heads, wl.rows, wl.head_dim)
-    emu = RingEmulator(kv[next(iter(kv))][0].shape, inp.q.dtype, compute_stream=compute)
+    emu = RingEmulator(kv[next(iter(kv))][0].shape, inp.q.dtype, compute_stream=compute, staging=staging)
     emu.free_hook = free_hook
     o = torch.empty((1, *st.o.shape[1:]), dtype=out_dtype, device="cuda")
     lse = torch.empty((1, *st.m.shape[1:]), dtype=torch.float32, device="cuda")
-    steps = ring_order(rank, wl.blocks) if order is None else list(order)
-    launched = sum(_lib.step_case(rank, j, wl.blocks, causal) != _lib.RA_CASE_SKIP for j in steps)
     pool = iter([Event(timing=True) for _ in range(2 * launched)])
     timers = []
     emu.run(st, inp.q, lambda j: kv[j], rank, wl.blocks, causal, wl.scale, order=order,

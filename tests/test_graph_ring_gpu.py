@@ -1,6 +1,8 @@
 """GPU: a ring captured once as a HIP graph and replayed (what bench.py does
 for its untimed rings) gives the eager ring's results bit for bit, on every
-replay, with eager rings, other work and synchronisations between replays."""
+replay, with eager rings, other work and synchronisations between replays;
+with the staging on a side stream and with the staging carried by the step
+launches."""
 import sys
 
 import pytest
@@ -29,12 +31,15 @@ def _say(msg):
 
 
 def _replays_match(one_ring, copy_stream, compute, outs):
+    """copy_stream None: the ring runs on the compute stream alone (staging
+    carried by the step launches)."""
     join = Event()
 
     def joined():
         one_ring()
-        join.record(copy_stream)
-        join.wait(compute)
+        if copy_stream is not None:
+            join.record(copy_stream)
+            join.wait(compute)
 
     joined()
     torch.cuda.synchronize()
@@ -67,8 +72,9 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("staging", ["side", "fused"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_captured_ring_replays_bit_identically(case):
+def test_captured_ring_replays_bit_identically(case, staging):
     name, dtype, heads, d, rows, P, rank, causal = case
     wl = synth.Workload(f"graph_{name}", 70 + rows, heads, d, rows, P, dtype, causal, (rank,))
     jobs = [(synth.ROLE_Q, rank)] + [(r, j) for j in range(P) for r in (synth.ROLE_K, synth.ROLE_V)]
@@ -78,18 +84,19 @@ def test_captured_ring_replays_bit_identically(case):
     ks = key_split_for(heads, rows, rows, causal)
     if ks > 1:
         kv = {j: (split_keys(k, ks), split_keys(v, ks)) for j, (k, v) in kv.items()}
-    _say(f"{name}: key split {ks}")
+    _say(f"{name}: key split {ks}, {staging} staging")
     compute = torch.cuda.Stream()
     st = _lib.State(ks, heads, rows, d)
-    emu = RingEmulator(kv[0][0].shape, q.dtype, compute_stream=compute)
+    emu = RingEmulator(kv[0][0].shape, q.dtype, compute_stream=compute, staging=staging)
     o = torch.empty((1, heads, rows, d), device="cuda")
     lse = torch.empty((1, heads, rows), device="cuda")
     _replays_match(lambda: emu.run(st, q, lambda j: kv[j], rank, P, causal, wl.scale,
                                    finalize_out=(o, lse), key_split=ks),
-                   emu.copy, compute, [o, lse])
+                   emu.copy if staging == "side" else None, compute, [o, lse])
 
 
-def test_captured_zigzag_ring_replays_bit_identically():
+@pytest.mark.parametrize("staging", ["side", "fused"])
+def test_captured_zigzag_ring_replays_bit_identically(staging):
     heads, d, rows, P, rank = 2, 128, 256, 4, 1
     wl = synth.Workload("graph_zigzag", 91, heads, d, rows, P, "bf16", True, (rank,))
     zw = synth.zigzag_workload(wl)
@@ -105,7 +112,7 @@ def test_captured_zigzag_ring_replays_bit_identically():
 
     compute = torch.cuda.Stream()
     states = [_lib.State(1, heads, zw.rows, d) for _ in range(2)]
-    zz = ZigzagRing(qs[0].shape, qs[0].dtype, compute_stream=compute)
+    zz = ZigzagRing(qs[0].shape, qs[0].dtype, compute_stream=compute, staging=staging)
     outs = [(torch.empty(st.o.shape, device="cuda"), torch.empty(st.m.shape, device="cuda")) for st in states]
     _replays_match(lambda: zz.run(states, qs, source, rank, P, True, wl.scale, finalize_outs=outs),
-                   zz.emu.copy, compute, [t for pair in outs for t in pair])
+                   zz.emu.copy if staging == "side" else None, compute, [t for pair in outs for t in pair])
