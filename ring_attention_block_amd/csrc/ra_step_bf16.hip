@@ -783,7 +783,10 @@ hipError_t launch(StepArgs a, hipStream_t s, const LaunchTiming &t) {
 // unless that grid leaves compute units idle as above (8 heads x 2048 rows:
 // 43 us with 4-wavefront workgroups against 49 us); at head_dim 64:
 // 4-wavefront workgroups, whose finer query tiles waste less work on the
-// masked triangle.
+// masked triangle.  Query blocks of at most 64 rows (decoding: one wavefront
+// has rows, the others only share the tile copies) take 4-wavefront workgroups
+// whatever the grid (16 new rows against 8 x 4096 keys x 32 heads: the fold
+// 96.7 us against 98.7 us with 8 wavefronts).
 constexpr int64_t kComputeUnits = 256;
 
 template <int D, bool kDiag>
@@ -792,7 +795,7 @@ hipError_t launch_d(const StepArgs &a, hipStream_t s, const LaunchTiming &t) {
     if (D == 64 || (int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s, t);
     return launch<D, kDiag, 8>(a, s, t);
   } else {
-    if ((int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits) return launch<D, kDiag, 4>(a, s, t);
+    if ((int64_t)a.bh * ((a.rows + 255) / 256) < kComputeUnits || a.rows <= 64) return launch<D, kDiag, 4>(a, s, t);
     return launch<D, kDiag, 8>(a, s, t);
   }
 }
