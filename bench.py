@@ -217,16 +217,20 @@ def timed_rings(args) -> int:
     return (args.steps + args.time_every - 1) // args.time_every
 
 
-def measured_traffic(wl, profile=TRAFFIC_PROFILE):
+def measured_traffic(wl, profile=TRAFFIC_PROFILE, require=None):
     """HBM bytes per full-step launch from a committed FETCH_SIZE/WRITE_SIZE summary.
 
-    Only for the workload the counters were taken on, and only while the
-    kernel source still hashes to the value recorded with them; else None.
+    Only for the workload the counters were taken on, only while the kernel
+    source still hashes to the value recorded with them, and only if every
+    `require` key is recorded there with the given value; else None.
     """
     if wl.name != DEFAULT_WORKLOAD:
         return None
-    f = profile_fields(os.path.basename(profile), ("traffic_bytes_per_launch",))
+    require = require or {}
+    f = profile_fields(os.path.basename(profile), ("traffic_bytes_per_launch", *require))
     if not f or "traffic_bytes_per_launch" not in f:
+        return None
+    if any(f.get(k) != str(v) for k, v in require.items()):
         return None
     return int(f["traffic_bytes_per_launch"])
 
@@ -290,12 +294,14 @@ def cpu_baseline_decode(wl, blocks, rq, target_s=15.0):
 
 def bench_decode(args, wl):
     """Decode: args.decode_rows query rows (the tokens after the sequence)
-    against the workload's P blocks as key/value shards, laid out as chunks
-    along the batch axis (ChunkedDecode: one ra_step launch over all shards
-    reading the one query block, one ra_merge_finalize).  Memory-bound: the figure of merit is
-    the key/value bytes read per second."""
+    against the workload's P blocks as key/value shards, each shard laid out
+    as S chunks of consecutive keys along the batch axis (decode.shard_chunks;
+    S from --decode-splits, by default decode.splits_for) (ChunkedDecode: one
+    ra_step launch over all chunks reading the one query block, one
+    ra_merge_finalize over the P*S partial states).  Memory-bound: the figure
+    of merit is the key/value bytes read per second."""
     import torch
-    from ring_attention_block_amd.decode import ChunkedDecode
+    from ring_attention_block_amd.decode import ChunkedDecode, shard_chunks, splits_for
     from ring_attention_block_amd.hip_events import Event
 
     rq, P, c = args.decode_rows, wl.blocks, wl.rows
@@ -307,11 +313,14 @@ def bench_decode(args, wl):
             else torch.from_numpy(x)
         return t.reshape(1, *x.shape).to(dev)
 
+    S = splits_for(P, wl.heads, c, rq) if args.decode_splits == "auto" else int(args.decode_splits)
+    if S < 1 or c % S:
+        raise SystemExit(f"--decode-splits {S} must divide the shard length {c}")
     q = to_dev(synth.block(wl, synth.ROLE_Q, P, rows=rq))   # the tokens after the cache
-    k = torch.cat([to_dev(blocks[(synth.ROLE_K, j)]) for j in range(P)], dim=0).contiguous()
-    v = torch.cat([to_dev(blocks[(synth.ROLE_V, j)]) for j in range(P)], dim=0).contiguous()
+    k = torch.cat([shard_chunks(to_dev(blocks[(synth.ROLE_K, j)]), S) for j in range(P)], dim=0).contiguous()
+    v = torch.cat([shard_chunks(to_dev(blocks[(synth.ROLE_V, j)]), S) for j in range(P)], dim=0).contiguous()
     compute = torch.cuda.Stream()
-    dec = ChunkedDecode(q.shape, P, dev, compute_stream=compute)
+    dec = ChunkedDecode(q.shape, P * S, dev, compute_stream=compute)
     o = torch.empty(q.shape, dtype=torch.float32, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     # The step kernel of one timed step in time_every carries timing events
@@ -338,9 +347,9 @@ def bench_decode(args, wl):
     kv_bytes = 2 * P * c * wl.heads * wl.head_dim * esize
     flops = 4 * wl.head_dim * wl.heads * rq * P * c
     # Algorithmic bytes of the fold launch: the cache and the query block as
-    # the P chunks' workgroups read it, the P partial states written (m, l, O
+    # the P*S chunks' workgroups read it, the P*S partial states written (m, l, O
     # in fp32; the fresh fold reads no state).
-    step_bytes = kv_bytes + P * wl.heads * rq * (wl.head_dim * esize + (wl.head_dim + 2) * 4)
+    step_bytes = kv_bytes + P * S * wl.heads * rq * (wl.head_dim * esize + (wl.head_dim + 2) * 4)
     step_ms = float(np.mean([a.elapsed_time(b) for a, b in timers]))
     achieved = step_bytes / (step_ms / 1e3) / 1e9
     peak = PEAK_HBM_BYTES / 1e9
@@ -352,13 +361,14 @@ def bench_decode(args, wl):
         "data": "synthetic (seeded N(0,1) blocks rounded to bf16, resident in HBM)",
         "config": {"workload": wl.name, "mode": "decode", "query_rows": rq, "shards": P,
                    "shard_rows": c, "heads": wl.heads, "head_dim": wl.head_dim,
-                   "layout": "shards as chunks along the batch axis",
+                   "splits_per_shard": S,
+                   "layout": f"each shard as {S} chunk(s) of {c // S} keys along the batch axis",
                    "kv_bytes": kv_bytes, "flop_per_step": flops,
                    "tflops": round(flops / (ms / 1e3) / 1e12, 2),
                    "pct_of_hbm_peak": round(100 * kv_bytes / (ms / 1e3) / PEAK_HBM_BYTES, 2)},
         "roofline": {"bound": "hbm", "kernel": "ra_step decode fold", "achieved": round(achieved, 1),
                      "peak": peak, "unit": "GB/s", "frac": round(achieved / peak, 4),
-                     "traffic": (measured_traffic(wl, DEC_TRAFFIC_PROFILE)
+                     "traffic": (measured_traffic(wl, DEC_TRAFFIC_PROFILE, {"splits_per_shard": S})
                                  if rq == DEC_TRAFFIC_ROWS else None),
                      "bytes_per_launch": step_bytes,
                      "avg_launch_ms": round(step_ms, 5), "launches": len(timers),
@@ -554,6 +564,10 @@ def main():
                     help="instead of the ring: decode this many query rows against the "
                          "workload's P blocks as key/value shards (all shards folded by one "
                          "launch along the batch axis, one merge-and-finalize launch)")
+    ap.add_argument("--decode-splits", default="auto",
+                    help="with --decode-rows: lay each shard out as this many chunks of "
+                         "consecutive keys along the batch axis (more workgroups per fold); "
+                         "auto: decode.splits_for")
     ap.add_argument("--backward", action="store_true",
                     help="instead of the forward ring: the rank's backward ring (D, then the "
                          "P gradient steps with dK, dV travelling with the blocks)")

@@ -77,6 +77,46 @@ class ShardedDecode:
                              lse_out=lse_out)
 
 
+def splits_for(shards: int, heads: int, shard_rows: int, query_rows: int,
+               compute_units: int = 256) -> int:
+    """Chunks per shard for ChunkedDecode.  A query block of at most 32 rows
+    (one wavefront's rows: the fold is a pure stream of the cache) takes the
+    fewest chunks that give the fold launch two workgroups per compute unit
+    (shards * splits * heads >= 2 * compute_units), among the divisors of the
+    shard length that leave chunks of at least 64 keys; longer query blocks,
+    and shards that already give enough workgroups, take 1.  Two workgroups per
+    unit keep twice the key/value tiles in flight; more chunks add partial
+    states to reduce.  Measured at 8 shards of 4096 keys and 32 heads (decode
+    step, ms, 1 chunk per shard against 2): 0.1058 / 0.0993 at 1 new row,
+    0.1063 / 0.1029 at 16, 0.1137 / 0.1130 at 64, 0.1790 / 0.1971 at 256;
+    4 and 8 chunks per shard were slower than 2 at 1 and 16 rows."""
+    if shards < 1 or heads < 1 or shard_rows < 1 or query_rows < 1:
+        raise ValueError("shards, heads, shard_rows and query_rows must be positive")
+    s = 1
+    if query_rows > 32:
+        return s
+    while shards * s * heads < 2 * compute_units:
+        nxt = next((x for x in range(s + 1, shard_rows + 1)
+                    if shard_rows % x == 0 and shard_rows // x >= 64), None)
+        if nxt is None:
+            break
+        s = nxt
+    return s
+
+
+def shard_chunks(x: torch.Tensor, splits: int) -> torch.Tensor:
+    """One shard [1, heads, rows, head_dim] as `splits` chunks of rows/splits
+    consecutive keys along the batch axis: [splits, heads, rows/splits,
+    head_dim] (a view; concatenate the shards' chunks along dim 0 and make the
+    result contiguous to get ChunkedDecode's cache layout)."""
+    if x.dim() != 4 or x.shape[0] != 1:
+        raise ValueError("a shard must be a [1, heads, rows, head_dim] tensor")
+    _, h, rows, d = x.shape
+    if splits < 1 or rows % splits:
+        raise ValueError(f"splits={splits} must divide the shard length {rows}")
+    return x.reshape(h, splits, rows // splits, d).transpose(0, 1)
+
+
 class ChunkedDecode:
     """Decode with the key/value cache laid out as chunks along the batch axis.
 

@@ -147,6 +147,41 @@ def test_chunked_decode(heads, d, rq, c, n, dtype):
     _say(f"  max|dO|={eo:.2e} max|dLSE|={el:.2e} (last head)")
 
 
+@pytest.mark.parametrize("heads,d,rq,c,P,splits,dtype", [
+    (2, 128, 16, 512, 4, 2, "bf16"),
+    (3, 64, 1, 384, 2, 3, "bf16"),
+    (2, 128, 5, 256, 3, 4, "f32"),
+])
+def test_chunked_decode_split_shards(heads, d, rq, c, P, splits, dtype):
+    """Each shard laid out as `splits` chunks of consecutive keys
+    (decode.shard_chunks, the layout bench.py's decode uses): ChunkedDecode over
+    the P * splits chunks against the oracle over the whole cache."""
+    from ring_attention_block_amd.decode import ChunkedDecode, shard_chunks
+    wl = synth.Workload(f"sdec_{dtype}_h{heads}_d{d}_q{rq}_c{c}_p{P}_s{splits}", 700 + rq + c, heads, d,
+                        c, P + 1, dtype, False, (P,))
+    _say(wl.name)
+    qh = synth.block(wl, synth.ROLE_Q, P, rows=rq)
+    kh = [synth.block(wl, synth.ROLE_K, j) for j in range(P)]
+    vh = [synth.block(wl, synth.ROLE_V, j) for j in range(P)]
+    q = to_device(qh, wl)
+    k = torch.cat([shard_chunks(to_device(x, wl), splits) for x in kh], dim=0).contiguous()
+    v = torch.cat([shard_chunks(to_device(x, wl), splits) for x in vh], dim=0).contiguous()
+    dec = ChunkedDecode(q.shape, P * splits)
+    o, lse = dec.run(q, k, v, wl.scale)
+    torch.cuda.synchronize()
+    to, tl = tol_for(wl)
+    kp, qp = np.arange(P * c), np.full(rq, P * c)
+    for hh in range(heads):
+        want_o, want_lse = dense.attention(
+            oracle_values(qh[hh:hh + 1], wl),
+            np.concatenate([oracle_values(x[hh:hh + 1], wl) for x in kh], axis=1),
+            np.concatenate([oracle_values(x[hh:hh + 1], wl) for x in vh], axis=1),
+            qp, kp, False, wl.scale)
+        eo = assert_close(o[0, hh].cpu().numpy(), want_o[0], to, f"head {hh} O")
+        el = assert_close(lse[0, hh].cpu().numpy(), want_lse[0], tl, f"head {hh} LSE")
+    _say(f"  max|dO|={eo:.2e} max|dLSE|={el:.2e} (last head)")
+
+
 MERGE_CASES = [
     # (output batch, parts, heads, rows, head_dim)
     (2, 5, 3, 37, 64),
