@@ -91,6 +91,17 @@ def software_versions() -> dict:
             "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count}
 
 
+def device_memory() -> dict:
+    """Peak device memory the run held through torch's caching allocator (the
+    library allocates nothing: every buffer of the emulated rank, the blocks
+    of the other ranks included, is a torch tensor)."""
+    import torch
+    return {"peak_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+            "peak_reserved_bytes": int(torch.cuda.max_memory_reserved()),
+            "note": "whole process: inputs of every emulated rank, receive buffers, states, "
+                    "outputs, graph pools"}
+
+
 COUNTER_PROFILE = "ra_step_bf16_causal_h32_d128_c4096_counters.md"
 COUNTER_KEYS = ("sclk_mhz", "mfma_busy_pct", "valu_busy_pct", "lds_bank_conflict_pct")
 
@@ -375,6 +386,7 @@ def bench_decode(args, wl):
                      "timed_steps": f"1 in {args.time_every} of the {args.steps} timed steps"},
         "compute_stream_ms": round(e0.elapsed_time(e1) / args.steps, 4),
         "env": software_versions(),
+        "memory": device_memory(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(wl, blocks, rq)
@@ -536,6 +548,7 @@ def bench_backward(args, wl, rank):
                            "diag": cases.count(_lib.RA_CASE_DIAG),
                            "full": cases.count(_lib.RA_CASE_FULL)}},
         "env": software_versions(),
+        "memory": device_memory(),
     }
     if not args.no_cpu_baseline and not zigzag:
         line["cpu_baseline"] = cpu_baseline_backward(wl, rank, blocks)
@@ -787,6 +800,7 @@ def main():
         "counters": ({"full": measured_counters("full"), "diag": measured_counters("diag")}
                      if wl.name == DEFAULT_WORKLOAD and args.partition == "contiguous" else None),
         "env": software_versions(),
+        "memory": device_memory(),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(step_wl, baseline_q, blocks)
