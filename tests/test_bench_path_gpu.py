@@ -164,6 +164,45 @@ def test_bench_path_causal_h32_d128_c4096_every_row(c2_inputs, rank):
     check_all(C2, o, lse, want, f"rank {rank}")
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rq", [1, 16, 64])
+def test_bench_decode_path_every_row(c2_inputs, rq):
+    """The decode step bench.py times (--decode-rows R): R query rows after the
+    sequence against the workload's 8 blocks as key/value shards, each shard
+    laid out as decode.splits_for chunks along the batch axis (2 at 1 and 16
+    rows, 1 at 64), one fold whose dispatch carries timing events and one
+    merge-and-finalize: every row and head against the oracle over all 32768
+    keys."""
+    from oracle import dense
+    from ring_attention_block_amd.decode import ChunkedDecode, shard_chunks, splits_for
+    from _helpers import oracle_values
+    inp, wl = c2_inputs, C2
+    P, c = wl.blocks, wl.rows
+    S = splits_for(P, wl.heads, c, rq)
+    _say(f"{wl.name}: decode {rq} rows, {S} chunk(s) per shard")
+    qh = synth.block(wl, synth.ROLE_Q, P, rows=rq)
+    q = to_device(qh, wl)
+    k = torch.cat([shard_chunks(inp.kv[j][0], S) for j in range(P)], dim=0).contiguous()
+    v = torch.cat([shard_chunks(inp.kv[j][1], S) for j in range(P)], dim=0).contiguous()
+    dec = ChunkedDecode(q.shape, P * S)
+    start, stop = Event(timing=True), Event(timing=True)
+    o, lse = dec.run(q, k, v, wl.scale, start=start, stop=stop)
+    torch.cuda.synchronize()
+    assert start.elapsed_time(stop) > 0
+    to, tl = tol_for(wl)
+    kp, qp = np.arange(P * c), np.full(rq, P * c)
+    eo = el = 0.0
+    for hh in range(wl.heads):
+        want_o, want_lse = dense.attention(
+            oracle_values(qh[hh:hh + 1], wl),
+            np.concatenate([oracle_values(inp.cache[(synth.ROLE_K, j)][hh:hh + 1], wl) for j in range(P)], axis=1),
+            np.concatenate([oracle_values(inp.cache[(synth.ROLE_V, j)][hh:hh + 1], wl) for j in range(P)], axis=1),
+            qp, kp, False, wl.scale)
+        eo = max(eo, assert_close(o[0, hh].cpu().numpy(), want_o[0], to, f"head {hh} O"))
+        el = max(el, assert_close(lse[0, hh].cpu().numpy(), want_lse[0], tl, f"head {hh} LSE"))
+    _say(f"  every row and head: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+
+
 C3 = synth.WORKLOADS["rescale_bf16_h8_d128_c2048_p16"]
 
 
