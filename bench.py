@@ -306,13 +306,14 @@ def cpu_baseline_decode(wl, blocks, rq, target_s=15.0):
 def bench_decode(args, wl):
     """Decode: args.decode_rows query rows (the tokens after the sequence)
     against the workload's P blocks as key/value shards, each shard laid out
-    as S chunks of consecutive keys along the batch axis (decode.shard_chunks;
+    as S chunks of consecutive keys along the batch axis (ring.split_keys;
     S from --decode-splits, by default decode.splits_for) (ChunkedDecode: one
     ra_step launch over all chunks reading the one query block, one
     ra_merge_finalize over the P*S partial states).  Memory-bound: the figure
     of merit is the key/value bytes read per second."""
     import torch
-    from ring_attention_block_amd.decode import ChunkedDecode, shard_chunks, splits_for
+    from ring_attention_block_amd.decode import ChunkedDecode, splits_for
+    from ring_attention_block_amd.ring import split_keys
     from ring_attention_block_amd.hip_events import Event
 
     rq, P, c = args.decode_rows, wl.blocks, wl.rows
@@ -328,8 +329,8 @@ def bench_decode(args, wl):
     if S < 1 or c % S:
         raise SystemExit(f"--decode-splits {S} must divide the shard length {c}")
     q = to_dev(synth.block(wl, synth.ROLE_Q, P, rows=rq))   # the tokens after the cache
-    k = torch.cat([shard_chunks(to_dev(blocks[(synth.ROLE_K, j)]), S) for j in range(P)], dim=0).contiguous()
-    v = torch.cat([shard_chunks(to_dev(blocks[(synth.ROLE_V, j)]), S) for j in range(P)], dim=0).contiguous()
+    k = torch.cat([split_keys(to_dev(blocks[(synth.ROLE_K, j)]), S) for j in range(P)], dim=0)
+    v = torch.cat([split_keys(to_dev(blocks[(synth.ROLE_V, j)]), S) for j in range(P)], dim=0)
     compute = torch.cuda.Stream()
     dec = ChunkedDecode(q.shape, P * S, dev, compute_stream=compute)
     o = torch.empty(q.shape, dtype=torch.float32, device=dev)

@@ -104,19 +104,6 @@ def splits_for(shards: int, heads: int, shard_rows: int, query_rows: int,
     return s
 
 
-def shard_chunks(x: torch.Tensor, splits: int) -> torch.Tensor:
-    """One shard [1, heads, rows, head_dim] as `splits` chunks of rows/splits
-    consecutive keys along the batch axis: [splits, heads, rows/splits,
-    head_dim] (a view; concatenate the shards' chunks along dim 0 and make the
-    result contiguous to get ChunkedDecode's cache layout)."""
-    if x.dim() != 4 or x.shape[0] != 1:
-        raise ValueError("a shard must be a [1, heads, rows, head_dim] tensor")
-    _, h, rows, d = x.shape
-    if splits < 1 or rows % splits:
-        raise ValueError(f"splits={splits} must divide the shard length {rows}")
-    return x.reshape(h, splits, rows // splits, d).transpose(0, 1)
-
-
 class ChunkedDecode:
     """Decode with the key/value cache laid out as chunks along the batch axis.
 

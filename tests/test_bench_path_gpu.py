@@ -174,7 +174,7 @@ def test_bench_decode_path_every_row(c2_inputs, rq):
     merge-and-finalize: every row and head against the oracle over all 32768
     keys."""
     from oracle import dense
-    from ring_attention_block_amd.decode import ChunkedDecode, shard_chunks, splits_for
+    from ring_attention_block_amd.decode import ChunkedDecode, splits_for
     from _helpers import oracle_values
     inp, wl = c2_inputs, C2
     P, c = wl.blocks, wl.rows
@@ -182,8 +182,8 @@ def test_bench_decode_path_every_row(c2_inputs, rq):
     _say(f"{wl.name}: decode {rq} rows, {S} chunk(s) per shard")
     qh = synth.block(wl, synth.ROLE_Q, P, rows=rq)
     q = to_device(qh, wl)
-    k = torch.cat([shard_chunks(inp.kv[j][0], S) for j in range(P)], dim=0).contiguous()
-    v = torch.cat([shard_chunks(inp.kv[j][1], S) for j in range(P)], dim=0).contiguous()
+    k = torch.cat([split_keys(inp.kv[j][0], S) for j in range(P)], dim=0)
+    v = torch.cat([split_keys(inp.kv[j][1], S) for j in range(P)], dim=0)
     dec = ChunkedDecode(q.shape, P * S)
     start, stop = Event(timing=True), Event(timing=True)
     o, lse = dec.run(q, k, v, wl.scale, start=start, stop=stop)

@@ -154,9 +154,10 @@ def test_chunked_decode(heads, d, rq, c, n, dtype):
 ])
 def test_chunked_decode_split_shards(heads, d, rq, c, P, splits, dtype):
     """Each shard laid out as `splits` chunks of consecutive keys
-    (decode.shard_chunks, the layout bench.py's decode uses): ChunkedDecode over
+    (ring.split_keys, the layout bench.py's decode uses): ChunkedDecode over
     the P * splits chunks against the oracle over the whole cache."""
-    from ring_attention_block_amd.decode import ChunkedDecode, shard_chunks
+    from ring_attention_block_amd.decode import ChunkedDecode
+    from ring_attention_block_amd.ring import split_keys
     wl = synth.Workload(f"sdec_{dtype}_h{heads}_d{d}_q{rq}_c{c}_p{P}_s{splits}", 700 + rq + c, heads, d,
                         c, P + 1, dtype, False, (P,))
     _say(wl.name)
@@ -164,8 +165,8 @@ def test_chunked_decode_split_shards(heads, d, rq, c, P, splits, dtype):
     kh = [synth.block(wl, synth.ROLE_K, j) for j in range(P)]
     vh = [synth.block(wl, synth.ROLE_V, j) for j in range(P)]
     q = to_device(qh, wl)
-    k = torch.cat([shard_chunks(to_device(x, wl), splits) for x in kh], dim=0).contiguous()
-    v = torch.cat([shard_chunks(to_device(x, wl), splits) for x in vh], dim=0).contiguous()
+    k = torch.cat([split_keys(to_device(x, wl), splits) for x in kh], dim=0)
+    v = torch.cat([split_keys(to_device(x, wl), splits) for x in vh], dim=0)
     dec = ChunkedDecode(q.shape, P * splits)
     o, lse = dec.run(q, k, v, wl.scale)
     torch.cuda.synchronize()

@@ -36,20 +36,3 @@ def test_splits_for_fills_two_workgroups_per_unit():
         assert rows % s == 0 and (s == 1 or rows // s >= 64)
     with pytest.raises(ValueError):
         splits_for(0, 32, 4096, 1)
-
-
-def test_shard_chunks_layout():
-    import torch
-    from ring_attention_block_amd.decode import shard_chunks
-    h, rows, d, s = 3, 12, 4, 4
-    x = torch.arange(h * rows * d, dtype=torch.float32).reshape(1, h, rows, d)
-    y = shard_chunks(x, s)
-    assert tuple(y.shape) == (s, h, rows // s, d)
-    for c in range(s):
-        for hh in range(h):
-            # chunk c holds keys c*rows/s .. (c+1)*rows/s - 1 of every head, in order
-            assert torch.equal(y[c, hh], x[0, hh, c * (rows // s):(c + 1) * (rows // s)])
-    with pytest.raises(ValueError):
-        shard_chunks(x, 5)
-    with pytest.raises(ValueError):
-        shard_chunks(x[0], 2)
