@@ -302,3 +302,87 @@ def test_bwd_batch_is_an_outer_head_axis(d, dtype):
             assert torch.equal(a, b), name
         else:
             assert float((a - b).abs().max()) <= 1e-5 * float(a.abs().max()), name
+
+
+@pytest.mark.timeout(1200)
+def test_bench_backward_path_every_head():
+    """The backward ring bench.py times (--backward): rank 7 of the causal
+    workload (32 heads, head_dim 128, 4096 rows per block, 8 blocks) on its
+    own compute stream: forward ring, finalize, ra_bwd_prepare (which also
+    zeroes dQ), then the backward ring with dK, dV travelling with the blocks
+    and timing events bound to every step (ra_bwd_step_timed).  dQ of the
+    rank and the rank's contribution to dK, dV of every block, on every head
+    and row, against the oracle (forward over the 8 visible blocks, D from its
+    output, then each block's backward from the oracle's LSE)."""
+    import concurrent.futures as cf
+    import contextlib
+    from ring_attention_block_amd.hip_events import Event
+    wl = synth.WORKLOADS["causal_bf16_h32_d128_c4096_p8"]
+    i, P, causal = 7, wl.blocks, True
+    jobs = [(synth.ROLE_Q, i), (synth.ROLE_DO, i)] + [(r, j) for j in range(P)
+                                                      for r in (synth.ROLE_K, synth.ROLE_V)]
+    host = gen_blocks(wl, jobs)
+    dev = {key: to_device(x, wl) for key, x in host.items()}
+    q, do = dev[(synth.ROLE_Q, i)], dev[(synth.ROLE_DO, i)]
+    kv = {j: (dev[(synth.ROLE_K, j)], dev[(synth.ROLE_V, j)]) for j in range(P)}
+    shape = tuple(q.shape)
+    compute = torch.cuda.Stream()
+    f32 = torch.float32
+    ring = RingEmulator(shape, q.dtype, "cuda", compute_stream=compute,
+                        extra_specs=[(shape, f32), (shape, f32)])
+    st = _lib.State(*shape)
+    ring.run(st, q, lambda j: kv[j], i, P, causal, wl.scale)
+    o, lse = _lib.finalize(st, f32, compute)
+    grads = {j: (torch.zeros(shape, dtype=f32, device="cuda"), torch.zeros(shape, dtype=f32, device="cuda"))
+             for j in range(P)}
+    dq = torch.full(shape, float("nan"), dtype=f32, device="cuda")   # ra_bwd_prepare zeroes it
+    delta = torch.empty(shape[:3], dtype=f32, device="cuda")
+    _lib.bwd_prepare(o, do, delta, stream=compute, dq=dq)
+    timers = []
+    pool = iter([Event(timing=True) for _ in range(2 * P)])
+    _say(f"  {wl.name} rank {i}: backward ring as bench.py runs it")
+    ring.run_backward(q, do, lse, delta, dq, lambda j: (kv[j][0], kv[j][1], grads[j][0], grads[j][1]),
+                      i, P, causal, wl.scale, step_timers=timers, timer_events=pool)
+    torch.cuda.synchronize()
+    assert len(timers) == P and all(a.elapsed_time(b) > 0 for _, a, b in timers)
+    got_dq = dq[0].cpu().numpy()
+    got_dk = {j: grads[j][0][0].cpu().numpy() for j in range(P)}
+    got_dv = {j: grads[j][1][0].cpu().numpy() for j in range(P)}
+    for t in [got_dq] + list(got_dk.values()) + list(got_dv.values()):
+        assert np.isfinite(t).all()
+
+    qf, dof = oracle_values(host[(synth.ROLE_Q, i)], wl), oracle_values(host[(synth.ROLE_DO, i)], wl)
+    kf = {j: oracle_values(host[(synth.ROLE_K, j)], wl) for j in range(P)}
+    vf = {j: oracle_values(host[(synth.ROLE_V, j)], wl) for j in range(P)}
+    qpos = dense.ring_positions(i, wl.rows)
+
+    def one_head(hd):
+        sl = slice(hd, hd + 1)
+        kall = np.concatenate([kf[j][sl] for j in range(P)], axis=1)
+        vall = np.concatenate([vf[j][sl] for j in range(P)], axis=1)
+        kpos_all = np.concatenate([dense.ring_positions(j, wl.rows) for j in range(P)])
+        o_h, lse_h = dense.attention(qf[sl], kall, vall, qpos, kpos_all, causal, wl.scale)
+        d_h = backward.row_dot(dof[sl], o_h)
+        wq = np.zeros_like(qf[sl])
+        wk, wv = {}, {}
+        for j in range(P):
+            bq, wk[j], wv[j] = backward.block_backward(qf[sl], kf[j][sl], vf[j][sl], dof[sl], lse_h, d_h,
+                                                       qpos, dense.ring_positions(j, wl.rows), causal,
+                                                       wl.scale)
+            wq = wq + bq
+        return wq[0], {j: wk[j][0] for j in wk}, {j: wv[j][0] for j in wv}
+
+    try:
+        from threadpoolctl import threadpool_limits
+        one_blas_thread = threadpool_limits(limits=1)
+    except ImportError:       # pragma: no cover
+        one_blas_thread = contextlib.nullcontext()
+    _say(f"  oracle backward over {wl.heads} heads")
+    with one_blas_thread, cf.ThreadPoolExecutor(max_workers=16) as ex:
+        want = list(ex.map(one_head, range(wl.heads)))
+    wq = np.stack([w[0] for w in want])
+    e = [_close(got_dq, wq, wl, "rank 7 dQ")]
+    for j in range(P):
+        e.append(_close(got_dk[j], np.stack([w[1][j] for w in want]), wl, f"block {j} dK"))
+        e.append(_close(got_dv[j], np.stack([w[2][j] for w in want]), wl, f"block {j} dV"))
+    _say(f"  every head and row: max rel err {max(e):.1e} (dQ {e[0]:.1e})")
