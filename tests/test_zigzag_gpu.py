@@ -194,3 +194,71 @@ def test_zigzag_fused_init_finalize_is_bit_identical(heads, d, rows, P, dtype, c
         torch.cuda.synchronize()
         for (o, l), (wo, wlse) in zip(outs, want):
             assert torch.equal(o, wo) and torch.equal(l, wlse), (rank, causal)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rank", [0])
+def test_bench_zigzag_path_every_row(rank):
+    """The zigzag ring bench.py times (--partition zigzag) at the headline
+    shape (32 heads, d = 128, 4096 tokens per rank in two pieces of 2048, 8
+    ranks): its own compute stream, the staging mode staging_for picks (the
+    next visit's copies carried by the piece products), init and finalize
+    fused into the first and last launched product, timing events on every
+    launch.  Both pieces, every row and head, against the oracle.  Every rank
+    runs the same launch sequence shape (the partition balances them); rank 0
+    is checked in full (about 100 s of oracle work), ranks 0 and 7 on sampled
+    rows by test_zigzag_headline_shape_sampled_rows."""
+    import concurrent.futures as cf
+    import contextlib
+    from ring_attention_block_amd.hip_events import Event
+    from ring_attention_block_amd.ring import staging_for, zigzag_plan
+    wl = synth.WORKLOADS["causal_bf16_h32_d128_c4096_p8"]
+    sub = synth.zigzag_workload(wl)
+    P = wl.blocks
+    mine = zigzag_blocks(rank, P)
+    cache = gen_blocks(sub, [(synth.ROLE_Q, b) for b in mine] +
+                       [(r, b) for b in range(2 * P) for r in (synth.ROLE_K, synth.ROLE_V)])
+    dev = {key: to_device(x, sub) for key, x in cache.items()}
+    qs = [dev[(synth.ROLE_Q, b)] for b in mine]
+
+    def source(j):
+        a, b = zigzag_blocks(j, P)
+        return (dev[(synth.ROLE_K, a)], dev[(synth.ROLE_K, b)],
+                dev[(synth.ROLE_V, a)], dev[(synth.ROLE_V, b)])
+
+    plan = zigzag_plan(rank, P, True)
+    skipped_visits = sum(all(c == _lib.RA_CASE_SKIP for _, _, c in prods) for _, prods in plan)
+    staging = staging_for(wl.heads, sub.rows, sub.rows, wl.head_dim, skipped_visits)
+    compute = torch.cuda.Stream()
+    states = [_lib.State(1, wl.heads, sub.rows, wl.head_dim) for _ in range(2)]
+    outs = [(torch.empty((1, wl.heads, sub.rows, wl.head_dim), dtype=torch.float32, device="cuda"),
+             torch.empty((1, wl.heads, sub.rows), dtype=torch.float32, device="cuda")) for _ in range(2)]
+    launched = sum(c != _lib.RA_CASE_SKIP for _, prods in plan for _, _, c in prods)
+    timers = []
+    pool = iter([Event(timing=True) for _ in range(2 * launched)])
+    ring = ZigzagRing(qs[0].shape, qs[0].dtype, "cuda", compute_stream=compute, staging=staging)
+    _say(f"{sub.name} rank {rank}: staging {staging}, {launched} launches")
+    ring.run(states, qs, source, rank, P, True, sub.scale, step_timers=timers, timer_events=pool,
+             finalize_outs=outs)
+    torch.cuda.synchronize()
+    assert len(timers) == launched
+
+    try:
+        from threadpoolctl import threadpool_limits
+        one_blas_thread = threadpool_limits(limits=1)
+    except ImportError:       # pragma: no cover
+        one_blas_thread = contextlib.nullcontext()
+    to, tl = tol_for(sub)
+    for piece, (o, lse) in zip(mine, outs):
+        def one(h, piece=piece):
+            return oracle_rank(sub, piece, range(2 * P), True, head_sel=[h], cache=cache)
+        parts = []
+        with one_blas_thread, cf.ThreadPoolExecutor(max_workers=16) as ex:
+            for h0 in range(0, wl.heads, 8):
+                parts += list(ex.map(one, range(h0, min(wl.heads, h0 + 8))))
+                _say(f"  piece {piece}: oracle heads {h0}..{min(wl.heads, h0 + 8) - 1}")
+        want_o = np.concatenate([p[0] for p in parts])
+        want_lse = np.concatenate([p[1] for p in parts])
+        eo = assert_close(o[0].cpu().numpy(), want_o, to, f"rank {rank} piece {piece} O")
+        el = assert_close(lse[0].cpu().numpy(), want_lse, tl, f"rank {rank} piece {piece} LSE")
+        _say(f"  piece {piece}, every row: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
