@@ -104,25 +104,38 @@ def plain_ring(inp, rank, causal, order=None, out_dtype=torch.float32):
     return o, lse
 
 
-def oracle_every_head(wl, rank, blocks, causal, cache, threads=16):
-    """oracle_rank over every head, the heads spread over a thread pool (numpy
-    releases the GIL in its products and exponentials; one BLAS thread each)."""
+def oracle_every_head(wl, rank, blocks, causal, cache, threads=16, row_block=2048):
+    """oracle_rank over every head and row, as (head, block of row_block query
+    rows) tasks on a thread pool (numpy releases the GIL in its products and
+    exponentials; one BLAS thread each), printing progress as they finish."""
     import contextlib
     try:
         from threadpoolctl import threadpool_limits
-        one_blas_thread = threadpool_limits(limits=1)
+        one_blas_thread = threadpool_limits(limits=1)   # applies now, restores on exit
     except ImportError:       # pragma: no cover
         one_blas_thread = contextlib.nullcontext()
     for key in [(synth.ROLE_Q, rank)] + [(r, j) for j in blocks for r in (synth.ROLE_K, synth.ROLE_V)]:
         if key not in cache:
             cache[key] = synth.block(wl, *key)
+    tasks = [(h, r0) for h in range(wl.heads) for r0 in range(0, wl.rows, row_block)]
 
-    def one(h):
-        return oracle_rank(wl, rank, blocks, causal, head_sel=[h], cache=cache)
+    def one(task):
+        h, r0 = task
+        rows = np.arange(r0, min(wl.rows, r0 + row_block))
+        return oracle_rank(wl, rank, blocks, causal, row_sel=rows, head_sel=[h], cache=cache)
 
+    parts = {}
     with one_blas_thread, cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        parts = list(ex.map(one, range(wl.heads)))
-    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+        futures = {ex.submit(one, t): t for t in tasks}
+        for n, fut in enumerate(cf.as_completed(futures), 1):
+            parts[futures[fut]] = fut.result()
+            if n % max(1, len(tasks) // 8) == 0 or n == len(tasks):
+                _say(f"    oracle: {n} of {len(tasks)} (head, row block) tasks")
+    o = np.stack([np.concatenate([parts[(h, r0)][0][0] for r0 in range(0, wl.rows, row_block)])
+                  for h in range(wl.heads)])
+    lse = np.stack([np.concatenate([parts[(h, r0)][1][0] for r0 in range(0, wl.rows, row_block)])
+                    for h in range(wl.heads)])
+    return o, lse
 
 
 def check_all(wl, o, lse, want, what, lse_slack=None):
@@ -201,6 +214,23 @@ def test_bench_decode_path_every_row(c2_inputs, rq):
         eo = max(eo, assert_close(o[0, hh].cpu().numpy(), want_o[0], to, f"head {hh} O"))
         el = max(el, assert_close(lse[0, hh].cpu().numpy(), want_lse[0], tl, f"head {hh} LSE"))
     _say(f"  every row and head: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+
+
+@pytest.mark.timeout(900)
+def test_bench_path_longshare_d64_every_row():
+    """The long-share ring bench.py times (--workload
+    longshare_bf16_h16_d64_c16384_p32): rank 31 folds all 32 blocks of 16384
+    keys at head_dim 64 (diagonal, then 31 full blocks) through the fused,
+    timed ring with side staging; every one of the 16384 rows x 16 heads
+    against the oracle over all 524288 keys."""
+    wl = synth.WORKLOADS["longshare_bf16_h16_d64_c16384_p32"]
+    rank = wl.ranks[-1]
+    inp = Inputs(wl, rank)
+    _say(f"{wl.name} rank {rank}: fused timed ring")
+    o, lse = bench_ring(inp, rank, True)
+    _say(f"  oracle over {wl.blocks} key blocks, every row")
+    want = oracle_every_head(wl, rank, list(range(wl.blocks)), True, inp.cache)
+    check_all(wl, o, lse, want, f"rank {rank}")
 
 
 C3 = synth.WORKLOADS["rescale_bf16_h8_d128_c2048_p16"]
