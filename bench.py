@@ -611,8 +611,9 @@ def main():
     import torch
     from ring_attention_block_amd import _lib
     from ring_attention_block_amd.hip_events import Event
-    from ring_attention_block_amd.ring import (RingEmulator, ZigzagRing, key_split_for, split_keys, staging_for,
-                                               zigzag_blocks, zigzag_plan)
+    from ring_attention_block_amd.ring import (RingEmulator, ZigzagRing, key_split_for, launch_pairs,
+                                               split_keys, staging_for, zigzag_blocks,
+                                               zigzag_fused_launches)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -669,37 +670,44 @@ def main():
     else:
         ks = 1
         # Zigzag: the sequence in 2P pieces of c/2 tokens; the rank holds
-        # pieces (rank, 2P-1-rank), and each visit is up to four piece products.
+        # pieces (rank, 2P-1-rank), both in one block in position order (and
+        # so does every visiting rank's block); each visit is one launch on
+        # row ranges of these blocks, the own visit one causal diagonal launch
+        # (ZigzagRing.run_block), split per piece where a fused init or
+        # finalize needs it.
         step_wl = synth.zigzag_workload(wl)
         mine = zigzag_blocks(rank, wl.blocks)
         blocks = generate(step_wl, rank, q_blocks=mine)
-        qs = [to_dev(blocks[(synth.ROLE_Q, b)], step_wl) for b in mine]
-        kv = {b: (to_dev(blocks[(synth.ROLE_K, b)], step_wl),
-                  to_dev(blocks[(synth.ROLE_V, b)], step_wl)) for b in range(step_wl.blocks)}
-
-        def source(j):
-            a, b = zigzag_blocks(j, wl.blocks)
-            return kv[a][0], kv[b][0], kv[a][1], kv[b][1]
-
-        states = [_lib.State(1, wl.heads, step_wl.rows, wl.head_dim, device=dev)
-                  for _ in range(2)]
-        cases = [c for _, prods in zigzag_plan(rank, wl.blocks, wl.causal) for _, _, c in prods]
-        skipped_visits = sum(all(c == _lib.RA_CASE_SKIP for _, _, c in prods)
-                             for _, prods in zigzag_plan(rank, wl.blocks, wl.causal))
-        staging = (staging_for(wl.heads, step_wl.rows, step_wl.rows, wl.head_dim, skipped_visits)
-                   if args.staging == "auto" else args.staging)
-        zz = ZigzagRing(qs[0].shape, qs[0].dtype, dev, compute_stream=compute, staging=staging)
-        copy_stream = zz.emu.copy if staging == "side" else None
+        q = torch.cat([to_dev(blocks[(synth.ROLE_Q, b)], step_wl) for b in mine], dim=2)
+        kv = {}
+        for j in range(wl.blocks):
+            pieces = zigzag_blocks(j, wl.blocks)
+            kv[j] = tuple(torch.cat([to_dev(blocks[(role, b)], step_wl) for b in pieces], dim=2)
+                          for role in (synth.ROLE_K, synth.ROLE_V))
+        states = [_lib.State(1, wl.heads, 2 * step_wl.rows, wl.head_dim, device=dev)]
+        fused = not args.unfused
+        zplan = zigzag_fused_launches(rank, wl.blocks, wl.causal)
+        if not fused:
+            from ring_attention_block_amd.ring import zigzag_launches
+            zplan = zigzag_launches(rank, wl.blocks, wl.causal)
+        launches = [l for _, ls in zplan for l in ls]
+        cases = [l[4] for l in launches]
         c2 = step_wl.rows
-        flops = 4 * wl.head_dim * wl.heads * (cases.count(_lib.RA_CASE_FULL) * c2 * c2 +
-                                              cases.count(_lib.RA_CASE_DIAG) * c2 * (c2 + 1) // 2)
+        launch_flops = [4 * wl.head_dim * wl.heads * launch_pairs(l, c2) for l in launches]
+        flops = sum(launch_flops)
+        # the visit with the least matrix work decides the staging mode
+        lightest = min(sum(launch_pairs(l, c2) for l in ls) for _, ls in zplan)
+        staging = (staging_for(wl.heads, lightest, 1, wl.head_dim, 0)
+                   if args.staging == "auto" else args.staging)
+        zz = ZigzagRing((1, wl.heads, c2, wl.head_dim), q.dtype, dev, compute_stream=compute,
+                        staging=staging)
+        copy_stream = zz.emu.copy if staging == "side" else None
         baseline_q = mine[1]
 
-        fused = not args.unfused
-
         def fold(timers, pool):
-            zz.run(states, qs, source, rank, wl.blocks, wl.causal, wl.scale,
-                   step_timers=timers, timer_events=pool, finalize_outs=outs if fused else None)
+            zz.run_block(states[0], q, lambda j: kv[j], rank, wl.blocks, wl.causal, wl.scale,
+                         step_timers=timers, timer_events=pool,
+                         finalize_out=outs[0] if fused else None)
 
     outs = [(torch.empty((1, *st.o.shape[1:]), dtype=torch.float32, device=dev),
              torch.empty((1, *st.m.shape[1:]), dtype=torch.float32, device=dev)) for st in states]
@@ -745,7 +753,15 @@ def main():
 
     full = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_FULL]
     diag = [a.elapsed_time(b) for c, a, b in timers if c == _lib.RA_CASE_DIAG]
-    if full:
+    if full and args.partition == "zigzag":
+        # launches of unequal sizes: the full launches' FLOP over their time
+        per = [(f, a.elapsed_time(b)) for (c, a, b), f in
+               zip(timers, launch_flops * (len(timers) // len(launch_flops)))
+               if c == _lib.RA_CASE_FULL]
+        dom_ms = float(np.mean([t for _, t in per]))
+        dom_flops = sum(f for f, _ in per) / len(per)
+        dom = "ra_step full (zigzag row ranges, mean launch)"
+    elif full:
         dom_ms, dom_flops, dom = float(np.mean(full)), full_step_flops(step_wl), "ra_step full"
     else:
         dom_ms = float(np.mean(diag))
@@ -757,8 +773,7 @@ def main():
     kernel_ms = n_full * (float(np.mean(full)) if full else 0.0) + \
         n_diag * (float(np.mean(diag)) if diag else 0.0)
     esize = 2 if wl.dtype == "bf16" else 4
-    per_visit = 2 if args.partition == "contiguous" else 4
-    staged = (wl.blocks - 1) * per_visit * wl.heads * step_wl.rows * wl.head_dim * esize
+    staged = (wl.blocks - 1) * 2 * wl.heads * wl.rows * wl.head_dim * esize
 
     line = {
         "metric": (f"{'causal' if wl.causal else 'non-causal'} {wl.dtype} ring-step attention "

@@ -22,8 +22,9 @@
  *   - Tensors are dense row-major: q and o are [batch, heads, rows,
  *     head_dim], k and v [batch, heads, kv_rows, head_dim]; m, l and lse are
  *     [batch, heads, rows].  Every non-empty tensor pointer must be 16-byte
- *     aligned, except the state's m and l, which need 4 bytes (so that a
- *     batch slice of a state is itself a valid state).
+ *     aligned, except the per-row vectors (the state's m and l, and lse),
+ *     which need 4 bytes (so that a batch or row slice of a state or of an
+ *     output is itself valid).
  *   - Every call is asynchronous and ordered on `stream` (0 = the null
  *     stream); no call synchronises.  Buffers must stay valid and unmodified
  *     until the stream has passed the call.
@@ -162,7 +163,8 @@ ra_status ra_step(ra_state *st, const void *q, const void *k, const void *v, ra_
  *              along the batch axis, without copying the query block per
  *              chunk); the result is that of a q repeated along the batch.
  *   o_out, out_dtype, lse_out   as in ra_finalize (used with
- *              RA_STEP_FINALIZE only; either may be NULL; 16-byte aligned).
+ *              RA_STEP_FINALIZE only; either may be NULL; o_out 16-byte,
+ *              lse_out 4-byte aligned).
  * A step that folds nothing (a skipped causal block, kv_rows == 0) still
  * applies its flags, by enqueueing ra_state_init and ra_finalize.
  */
@@ -232,7 +234,8 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
  * The same result as merging the parts pairwise with ra_lse_merge (any
  * order) and finalizing, up to rounding.  A row no part saw gives o_out = 0
  * and lse_out = -inf.  parts must divide batch (RA_ERR_INVALID_ARG
- * otherwise); outputs 16-byte aligned.  The state is not modified.
+ * otherwise); o_out 16-byte, lse_out 4-byte aligned.  The state is not
+ * modified.
  */
 ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_dtype out_dtype,
                             float *lse_out, hipStream_t stream);
@@ -305,6 +308,35 @@ ra_status ra_step_staged(ra_state *st, const void *q, const void *k, const void 
                          int32_t num_blocks, int32_t causal, float scale, uint32_t flags,
                          void *o_out, ra_dtype out_dtype, float *lse_out, const ra_copy *copies,
                          int32_t n_copies, hipEvent_t start, hipEvent_t stop, hipStream_t stream);
+
+/*
+ * ra_step_staged on tensors whose (batch, head) entries are not packed: the
+ * entry e = b * heads + h of q, of the state's m, l and o and of o_out and
+ * lse_out starts at row e * row_stride (element e * row_stride * head_dim of
+ * q, o and o_out, element e * row_stride of m, l and lse_out), that of k and v
+ * at row e * kv_row_stride; within an entry rows stay packed.  One launch can
+ * so fold a row range of a longer block (query rows [r0, r0 + rows) of every
+ * head: pointers advanced by r0 rows, row_stride the longer block's rows)
+ * against a row range of another.  The zigzag partition of "Ring
+ * Attention：...", section "Causal Attention 让环不再完全对称", uses it: a
+ * rank keeps its two sub-blocks in position order, one block per head, and
+ * every visit of another rank's two sub-blocks is one such launch (the later
+ * sub-block against both, or both against the earlier one), the visit of its
+ * own one causal diagonal launch.
+ *   row_stride     >= st->rows (st->rows: packed), else RA_ERR_INVALID_ARG
+ *   kv_row_stride  >= kv_rows (kv_rows: packed), else RA_ERR_INVALID_ARG
+ * The overlap checks compare each buffer's whole extent, from the first row of
+ * entry 0 to the end of the last entry.  RA_STEP_FRESH and RA_STEP_FINALIZE
+ * on a call that folds nothing (skipped block, kv_rows == 0) with row_stride
+ * != st->rows return RA_ERR_UNSUPPORTED (the state kernels take packed
+ * states).  Everything else, and the error behaviour, as ra_step_staged.
+ */
+ra_status ra_step_strided(ra_state *st, int32_t row_stride, const void *q, const void *k,
+                          const void *v, ra_dtype in_dtype, int32_t kv_rows, int32_t kv_row_stride,
+                          int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
+                          float scale, uint32_t flags, void *o_out, ra_dtype out_dtype,
+                          float *lse_out, const ra_copy *copies, int32_t n_copies, hipEvent_t start,
+                          hipEvent_t stop, hipStream_t stream);
 
 /*
  * Backward, per-row term ("Ring Attention：...", section "Backward 需要让梯度也

@@ -21,7 +21,7 @@ RA_STAGE_ALONE = 1
 
 # Every symbol include/ra.h declares.
 EXPORTS = ("ra_state_init", "ra_step_case", "ra_step", "ra_step_ex", "ra_step_timed", "ra_step_staged",
-           "ra_lse_merge",
+           "ra_step_strided", "ra_lse_merge",
            "ra_finalize", "ra_merge_finalize", "ra_stage_block", "ra_stage_block_ex", "ra_bwd_prepare", "ra_bwd_step",
            "ra_bwd_step_timed",
            "ra_status_string", "ra_last_error")
@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
             "ra_step_staged": (ctypes.c_int, [sp, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32,
                                               f32, ctypes.c_uint32, vp, ctypes.c_int, vp,
                                               ctypes.POINTER(RaCopy), i32, vp, vp, vp]),
+            "ra_step_strided": (ctypes.c_int, [sp, i32, vp, vp, vp, ctypes.c_int, i32, i32, i32, i32,
+                                               i32, i32, f32, ctypes.c_uint32, vp, ctypes.c_int, vp,
+                                               ctypes.POINTER(RaCopy), i32, vp, vp, vp]),
             "ra_lse_merge": (ctypes.c_int, [sp, sp, vp]),
             "ra_finalize": (ctypes.c_int, [sp, vp, ctypes.c_int, vp, vp]),
             "ra_merge_finalize": (ctypes.c_int, [sp, i32, vp, ctypes.c_int, vp, vp]),
@@ -187,6 +190,19 @@ class State:
     @property
     def shape(self):
         return (self.c.batch, self.c.heads, self.c.rows, self.c.head_dim)
+
+    def row_slice(self, start: int, count: int) -> "State":
+        """The state of rows [start, start + count) of every (batch, head)
+        entry, sharing memory: a strided state for step_strided."""
+        b, h, r, d = self.shape
+        if start < 0 or count < 0 or start + count > r:
+            raise ValueError(f"row slice [{start}, {start + count}) outside [0, {r})")
+        view = State.__new__(State)
+        view.m = self.m[:, :, start:start + count]
+        view.l = self.l[:, :, start:start + count]
+        view.o = self.o[:, :, start:start + count]
+        view.c = RaState(b, h, count, d, view.m.data_ptr(), view.l.data_ptr(), view.o.data_ptr())
+        return view
 
     def batch_slice(self, start: int, count: int) -> "State":
         """The state of batch entries [start, start + count), sharing memory."""
@@ -327,6 +343,82 @@ def step_staged_checked(st: State, q, k, v, q_block: int, kv_block: int, num_blo
                                 k.shape[2], q_block, kv_block, num_blocks, int(causal), float(scale),
                                 int(flags), _ptr(o_out), out_code, _ptr(lse_out), _copy_array(copies),
                                 len(copies), _event(start), _event(stop), _stream(stream)))
+    return step_case(q_block, kv_block, num_blocks, causal)
+
+
+def _row_stride(name: str, t, shape, dtypes) -> int:
+    """Rows between consecutive (batch, head) entries of t, a [batch, heads,
+    rows] or [batch, heads, rows, head_dim] tensor of exactly `shape` whose
+    rows are packed within each entry and whose entries are evenly spaced
+    (a packed tensor, or a row range of a longer one); raises otherwise."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {[str(d) for d in dtypes]}, got {t.dtype}")
+    b, h, r = shape[:3]
+    inner = shape[3] if len(shape) == 4 else 1
+    st = t.stride()
+    if len(shape) == 4 and inner > 1 and st[3] != 1:
+        raise ValueError(f"{name}: elements of a row must be packed")
+    if r > 1 and st[2] != inner:
+        raise ValueError(f"{name}: rows of a (batch, head) entry must be packed")
+    if h > 1:
+        entry = st[1]
+        if b > 1 and st[0] != h * entry:
+            raise ValueError(f"{name}: (batch, head) entries must be evenly spaced")
+    elif b > 1:
+        entry = st[0]
+    else:
+        entry = r * inner
+    if entry % inner or entry // inner < r:
+        raise ValueError(f"{name}: (batch, head) entries overlap or are misaligned")
+    return entry // inner
+
+
+def check_step_strided(st: State, q, k, v, flags: int = 0, o_out=None, lse_out=None) -> tuple:
+    """The checks step_strided() makes before any library call; returns
+    (row_stride, kv_row_stride)."""
+    b, h, r, d = st.shape
+    rs = _row_stride("state.m", st.m, (b, h, r), _F32)
+    for name, t in (("state.l", st.l), ("state.o", st.o)):
+        if _row_stride(name, t, t.shape, _F32) != rs or tuple(t.shape[:3]) != (b, h, r):
+            raise ValueError(f"{name} does not share the layout of state.m")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share one dtype")
+    dts = (torch.bfloat16, torch.float32)
+    q_batch = 1 if flags & RA_STEP_Q_BROADCAST else b
+    if _row_stride("q", q, (q_batch, h, r, d), dts) != rs and q_batch * h > 1:
+        raise ValueError("q must have the state's row stride")
+    if k.dim() != 4 or tuple(k.shape) != tuple(v.shape) or (k.shape[0], k.shape[1], k.shape[3]) != (b, h, d):
+        raise ValueError(f"k, v shapes do not fit the state: {tuple(k.shape)} {tuple(v.shape)}")
+    kvs = _row_stride("k", k, k.shape, dts)
+    if _row_stride("v", v, v.shape, dts) != kvs:
+        raise ValueError("k and v must share one row stride")
+    if flags & RA_STEP_FINALIZE:
+        if o_out is not None and _row_stride("o_out", o_out, (b, h, r, d), _IO_DTYPES) != rs and b * h > 1:
+            raise ValueError("o_out must have the state's row stride")
+        if lse_out is not None and _row_stride("lse_out", lse_out, (b, h, r), _F32) != rs and b * h > 1:
+            raise ValueError("lse_out must have the state's row stride")
+    _on_gpu(q=q, k=k, v=v, o_out=o_out, lse_out=lse_out, m=st.m, l=st.l, o=st.o)
+    return rs, kvs
+
+
+def step_strided(st: State, q, k, v, q_block: int, kv_block: int, num_blocks: int, causal: bool,
+                 scale: float, copies=(), stream=None, flags: int = 0, o_out=None, lse_out=None,
+                 start=None, stop=None) -> int:
+    """step_staged() on row ranges of longer blocks (ra_step_strided): q, the
+    state (State.row_slice) and the outputs share one row stride, k and v
+    another; every operand may also be packed.  Returns the causal case."""
+    rs, kvs = check_step_strided(st, q, k, v, flags, o_out, lse_out)
+    check_copies(copies)
+    out_code = RA_BF16 if o_out is not None and o_out.dtype == torch.bfloat16 else RA_F32
+    _check(lib().ra_step_strided(ctypes.byref(st.c), rs, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 _dtype_code(q), k.shape[2], kvs, q_block, kv_block, num_blocks,
+                                 int(causal), float(scale), int(flags), _ptr(o_out), out_code,
+                                 _ptr(lse_out), _copy_array(copies), len(copies), _event(start),
+                                 _event(stop), _stream(stream)))
     return step_case(q_block, kv_block, num_blocks, causal)
 
 

@@ -216,10 +216,27 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
                     ra_dtype in_dtype, int32_t kv_rows, int32_t q_block, int32_t kv_block,
                     int32_t num_blocks, int32_t causal, float scale, uint32_t flags, void *o_out,
                     ra_dtype out_dtype, float *lse_out, hipEvent_t start, hipEvent_t stop,
-                    hipStream_t stream, const ra_copy *copies = nullptr, int32_t n_copies = 0) {
+                    hipStream_t stream, const ra_copy *copies = nullptr, int32_t n_copies = 0,
+                    int64_t row_stride = -1, int64_t kv_row_stride = -1) {
+  // row_stride, kv_row_stride: rows between consecutive (batch, head) entries
+  // of q / the state / the outputs and of k / v; -1 = packed (rows, kv_rows).
   int64_t n = 0;
   ra_status s = check_state(st, name, &n);
   if (s != RA_OK) return s;
+  const bool strided = row_stride >= 0 || kv_row_stride >= 0;
+  const int64_t rs = row_stride < 0 ? st->rows : row_stride;
+  const int64_t kvs = kv_row_stride < 0 ? (kv_rows > 0 ? kv_rows : 0) : kv_row_stride;
+  if (rs < st->rows)
+    return fail(RA_ERR_INVALID_ARG, "%s: row_stride=%lld is below rows=%d", name, (long long)rs, st->rows);
+  if (kvs < kv_rows)
+    return fail(RA_ERR_INVALID_ARG, "%s: kv_row_stride=%lld is below kv_rows=%d", name,
+                (long long)kvs, kv_rows);
+  const int64_t n_bh = (int64_t)st->batch * st->heads;
+  if (n_bh * (rs > kvs ? rs : kvs) > ((int64_t)1 << 40) / st->head_dim)
+    return fail(RA_ERR_INVALID_ARG, "%s: strided extent is too large", name);
+  // Rows from the first row of the first (batch, head) entry to the end of the
+  // last one: the extent of each buffer that the overlap checks compare.
+  const int64_t ext = n_bh > 0 ? (n_bh - 1) * rs + st->rows : 0;
   const int32_t c = ra_step_case(q_block, kv_block, num_blocks, causal);
   if (c < 0) return (ra_status)c;
   if (in_dtype != RA_F32 && in_dtype != RA_BF16)
@@ -240,8 +257,8 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   if (flags & RA_STEP_FINALIZE) {
     if (out_dtype != RA_F32 && out_dtype != RA_BF16)
       return fail(RA_ERR_INVALID_ARG, "%s: out_dtype=%d is not RA_F32 or RA_BF16", name, (int)out_dtype);
-    if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
-      return fail(RA_ERR_INVALID_ARG, "%s: outputs must be 16-byte aligned", name);
+    if ((o_out && !aligned16(o_out)) || (lse_out && !aligned4(lse_out)))
+      return fail(RA_ERR_INVALID_ARG, "%s: o_out must be 16-byte aligned, lse_out 4-byte aligned", name);
   }
   if (n > 0) {
     if (!q) return fail(RA_ERR_INVALID_ARG, "%s: NULL q", name);
@@ -252,13 +269,19 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
         return fail(RA_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned", name);
     }
     const int64_t es = in_dtype == RA_BF16 ? 2 : 4, d = st->head_dim;
-    const int64_t q_rows = (flags & RA_STEP_Q_BROADCAST) ? (int64_t)st->heads * st->rows : n;
-    const int64_t kv_n = (int64_t)st->batch * st->heads * kv_rows;
+    const int64_t q_rows = (flags & RA_STEP_Q_BROADCAST) ? (st->heads - 1) * rs + st->rows : ext;
+    const int64_t kv_n = kv_rows > 0 ? (n_bh - 1) * kvs + kv_rows : 0;
     const Span in[] = {{q, q_rows * d * es, "q"}, {k, kv_n * d * es, "k"}, {v, kv_n * d * es, "v"}};
-    const Span state[] = {{st->m, n * 4, "state m"}, {st->l, n * 4, "state l"},
-                          {st->o, n * d * 4, "state o"}};
-    const Span out[] = {{o_out, n * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"},
-                        {lse_out, n * 4, "lse_out"}};
+    const Span state[] = {{st->m, ext * 4, "state m"}, {st->l, ext * 4, "state l"},
+                          {st->o, ext * d * 4, "state o"}};
+    const Span out[] = {{o_out, ext * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"},
+                        {lse_out, ext * 4, "lse_out"}};
+    if (strided) {
+      for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+          if (overlap(state[i], state[j]))
+            return fail(RA_ERR_INVALID_ARG, "%s: %s and %s overlap", name, state[i].name, state[j].name);
+    }
     if (flags & RA_STEP_FINALIZE) {
       const Span rd[] = {in[0], in[1], in[2], state[0], state[1], state[2]};
       s = check_disjoint(name, out, rd);
@@ -282,6 +305,9 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   if (n == 0 || c == RA_CASE_SKIP || kv_rows == 0) {
     // Nothing to fold: the flags still take effect through the state kernels,
     // and the timing events bracket whatever they enqueue.
+    if (n > 0 && strided && rs != st->rows && (flags & (RA_STEP_FRESH | RA_STEP_FINALIZE)))
+      return fail(RA_ERR_UNSUPPORTED,
+                  "%s: RA_STEP_FRESH or RA_STEP_FINALIZE on a strided state that folds nothing", name);
     if (start) {
       (void)hipGetLastError();
       const hipError_t e = hipEventRecord(start, stream);
@@ -312,6 +338,8 @@ ra_status step_impl(const char *name, ra_state *st, const void *q, const void *k
   a.o = st->o;
   a.rows = st->rows;
   a.kv_rows = kv_rows;
+  a.row_stride = (int32_t)rs;
+  a.kv_stride = (int32_t)kvs;
   a.bh = st->batch * st->heads;
   a.q_bh = (flags & RA_STEP_Q_BROADCAST) ? st->heads : a.bh;
   a.scale_log2 = scale * 1.442695040888963407f;
@@ -377,6 +405,23 @@ ra_status ra_step_staged(ra_state *st, const void *q, const void *k, const void 
                    n_copies);
 }
 
+ra_status ra_step_strided(ra_state *st, int32_t row_stride, const void *q, const void *k,
+                          const void *v, ra_dtype in_dtype, int32_t kv_rows, int32_t kv_row_stride,
+                          int32_t q_block, int32_t kv_block, int32_t num_blocks, int32_t causal,
+                          float scale, uint32_t flags, void *o_out, ra_dtype out_dtype,
+                          float *lse_out, const ra_copy *copies, int32_t n_copies, hipEvent_t start,
+                          hipEvent_t stop, hipStream_t stream) {
+  if (row_stride < 0 || kv_row_stride < 0)
+    return fail(RA_ERR_INVALID_ARG, "ra_step_strided: negative row stride (%d, %d)", row_stride,
+                kv_row_stride);
+  if (n_copies < 0 || n_copies > RA_MAX_STEP_COPIES)
+    return fail(RA_ERR_INVALID_ARG, "ra_step_strided: n_copies=%d (0 to %d)", n_copies, RA_MAX_STEP_COPIES);
+  if (n_copies > 0 && !copies) return fail(RA_ERR_INVALID_ARG, "ra_step_strided: NULL copies");
+  return step_impl("ra_step_strided", st, q, k, v, in_dtype, kv_rows, q_block, kv_block, num_blocks,
+                   causal, scale, flags, o_out, out_dtype, lse_out, start, stop, stream, copies,
+                   n_copies, row_stride, kv_row_stride);
+}
+
 ra_status ra_lse_merge(ra_state *dst, const ra_state *src, hipStream_t stream) {
   int64_t nd = 0, ns = 0;
   ra_status s = check_state(dst, "ra_lse_merge dst", &nd);
@@ -407,8 +452,8 @@ ra_status ra_finalize(const ra_state *st, void *o_out, ra_dtype out_dtype, float
     return fail(RA_ERR_INVALID_ARG, "ra_finalize: out_dtype=%d is not RA_F32 or RA_BF16",
                 (int)out_dtype);
   if (n == 0 || (!o_out && !lse_out)) return ok();
-  if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
-    return fail(RA_ERR_INVALID_ARG, "ra_finalize: outputs must be 16-byte aligned");
+  if ((o_out && !aligned16(o_out)) || (lse_out && !aligned4(lse_out)))
+    return fail(RA_ERR_INVALID_ARG, "ra_finalize: o_out must be 16-byte aligned, lse_out 4-byte aligned");
   {
     const int64_t d = st->head_dim;
     const Span w[] = {{o_out, n * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"}, {lse_out, n * 4, "lse_out"}};
@@ -434,8 +479,8 @@ ra_status ra_merge_finalize(const ra_state *st, int32_t parts, void *o_out, ra_d
     return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: parts=%d must be >= 1 and divide batch=%d",
                 (int)parts, (int)st->batch);
   if (n == 0 || (!o_out && !lse_out)) return ok();
-  if ((o_out && !aligned16(o_out)) || (lse_out && !aligned16(lse_out)))
-    return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: outputs must be 16-byte aligned");
+  if ((o_out && !aligned16(o_out)) || (lse_out && !aligned4(lse_out)))
+    return fail(RA_ERR_INVALID_ARG, "ra_merge_finalize: o_out must be 16-byte aligned, lse_out 4-byte aligned");
   {
     const int64_t d = st->head_dim, no = n / parts;
     const Span w[] = {{o_out, no * d * (out_dtype == RA_BF16 ? 2 : 4), "o_out"}, {lse_out, no * 4, "lse_out"}};

@@ -30,6 +30,9 @@ struct StepArgs {
   float *m, *l, *o;       // state
   int32_t rows;           // query rows of the block
   int32_t kv_rows;        // key/value rows of the visiting block (== rows for a diagonal block)
+  int32_t row_stride;     // rows between consecutive (batch, head) entries of q, the state and
+                          // the outputs (>= rows; rows for packed tensors)
+  int32_t kv_stride;      // the same for k and v (>= kv_rows)
   int32_t bh;             // batch * heads
   int32_t q_bh;           // (batch, head) entries of q: q entry of bh is bh % q_bh
   float scale_log2;       // score scale * log2(e): kernels work in base 2

@@ -305,10 +305,11 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   const int row = q0w + r;
   const bool row_ok = row < rows;
 
-  const size_t base = (size_t)bh * rows * D;
-  const size_t kv_base = (size_t)bh * kv_rows * D;
+  const size_t srow0 = (size_t)bh * a.row_stride;   // first state row of this (batch, head)
+  const size_t base = srow0 * D;
+  const size_t kv_base = (size_t)bh * a.kv_stride * D;
   const int q_bh = bh < a.q_bh ? bh : bh % a.q_bh;   // a query block shared along the batch
-  const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.q) + (size_t)q_bh * rows * D;
+  const uint16_t *__restrict__ Q = static_cast<const uint16_t *>(a.q) + (size_t)q_bh * a.row_stride * D;
   float *__restrict__ O = a.o + base;
   // The query rows and the state are read through buffer resources whose
   // range check returns 0 past the block end and, for the state, for every row
@@ -318,8 +319,8 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
   const uint32_t state_rows = fresh ? 0u : (uint32_t)rows;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q, (uint32_t)rows * T::kRowBytes);
   const __amdgpu_buffer_rsrc_t rso = make_rsrc(O, state_rows * (uint32_t)(D * 4));
-  const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a.m + (size_t)bh * rows, state_rows * 4u);
-  const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.l + (size_t)bh * rows, state_rows * 4u);
+  const __amdgpu_buffer_rsrc_t rsm = make_rsrc(a.m + srow0, state_rows * 4u);
+  const __amdgpu_buffer_rsrc_t rsl = make_rsrc(a.l + srow0, state_rows * 4u);
   const uint32_t blk_bytes = (uint32_t)kv_rows * T::kRowBytes;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const uint16_t *>(a.k) + kv_base, blk_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const uint16_t *>(a.v) + kv_base, blk_bytes);
@@ -695,7 +696,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
         *reinterpret_cast<float4 *>(O + ro + b * 32 + g * 8 + h * 4) = x;
       }
     if (h == 0) {
-      const size_t sr = (size_t)bh * rows + row;
+      const size_t sr = srow0 + row;
       a.m[sr] = rs.m_run * kLn2;
       a.l[sr] = l_tot * beta;
     }
@@ -727,7 +728,7 @@ __global__ void __launch_bounds__(64 * kW, 8 / kW) step_bf16_kernel(StepArgs a) 
       // m is rounded to fp32 before the add, as the stored state is.
 #pragma clang fp contract(off)
       const float m_nat = rs.m_run * kLn2;
-      a.lse_out[(size_t)bh * rows + row] = lr > 0.f ? m_nat + logf(lr) : -INFINITY;
+      a.lse_out[srow0 + row] = lr > 0.f ? m_nat + logf(lr) : -INFINITY;
     }
   }
   // The rest of this workgroup's slices of the carried copies (a workgroup

@@ -35,14 +35,14 @@ __global__ void __launch_bounds__(kThreads) step_f32_kernel(StepArgs a) {
   const int r = tid >> 2, part = tid & 3;
   const int row = qt * kRows + r;
   const bool row_ok = row < rows;
-  const size_t base = (size_t)bh * rows * D;
-  const size_t kv_base = (size_t)bh * kv_rows * D;
+  const size_t base = (size_t)bh * a.row_stride * D;
+  const size_t kv_base = (size_t)bh * a.kv_stride * D;
   const int q_bh = bh < a.q_bh ? bh : bh % a.q_bh;   // a query block shared along the batch
-  const float *__restrict__ Q = static_cast<const float *>(a.q) + (size_t)q_bh * rows * D;
+  const float *__restrict__ Q = static_cast<const float *>(a.q) + (size_t)q_bh * a.row_stride * D;
   const float *__restrict__ K = static_cast<const float *>(a.k) + kv_base;
   const float *__restrict__ V = static_cast<const float *>(a.v) + kv_base;
   float *__restrict__ O = a.o + base;
-  const size_t srow = (size_t)bh * rows + row;
+  const size_t srow = (size_t)bh * a.row_stride + row;
 
   const bool read_state = row_ok && !(a.flags & kStepFresh);
   float qv[kPart], ov[kPart];

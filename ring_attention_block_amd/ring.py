@@ -278,13 +278,18 @@ class RingEmulator:
         return e0, e1
 
     def step(self, st, q, k, v, i, j, num_blocks, causal, scale, case, step_timers=None,
-             timer_events=None, flags=0, out=(None, None), checked=False) -> None:
+             timer_events=None, flags=0, out=(None, None), checked=False, strided=False) -> None:
         """One ra_step (ra_step_ex with flags) on the compute stream; with
         step_timers (see run), ra_step_timed binds a pair of timing events to
         the step kernel's dispatch.  checked: the operands passed
-        _lib.check_step already (see run)."""
+        _lib.check_step already (see run).  strided: q, k, v, the state and
+        the outputs may be row ranges of longer blocks (ra_step_strided)."""
         e0, e1 = self.timer_pair(case, step_timers, timer_events)
         copies = self._take_copies(case)
+        if strided:
+            _lib.step_strided(st, q, k, v, i, j, num_blocks, causal, scale, copies, self.compute,
+                              flags=flags, o_out=out[0], lse_out=out[1], start=e0, stop=e1)
+            return
         if copies:
             launch = _lib.step_staged_checked if checked else _lib.step_staged
             launch(st, q, k, v, i, j, num_blocks, causal, scale, copies, self.compute, flags=flags,
@@ -395,6 +400,99 @@ class RingEmulator:
         return cases
 
 
+def zigzag_launches(rank: int, ranks: int, causal: bool) -> list:
+    """Per ring step: (visiting rank j, [(q_lo, q_n, kv_lo, kv_n, case)]), the
+    launches of ZigzagRing.run_block.  A rank's block holds its two sub-blocks
+    in position order (sub-block 0 the earlier), so do the visiting ones; a
+    launch folds query sub-blocks [q_lo, q_lo + q_n) against key/value
+    sub-blocks [kv_lo, kv_lo + kv_n) with case RA_CASE_FULL (no mask) or
+    RA_CASE_DIAG (the causal mask of the joined block, which is the mask of
+    its positions because they increase along it).  Under the causal mask a
+    visit of the rank's own block is one diagonal launch, of an earlier rank
+    one launch of both query sub-blocks against the earlier visiting
+    sub-block, of a later rank one launch of the later query sub-block
+    against both (zigzag_plan's pair cases, joined); pairs that join into
+    no such rectangle stay one launch each."""
+    F, D, S = _lib.RA_CASE_FULL, _lib.RA_CASE_DIAG, _lib.RA_CASE_SKIP
+    out = []
+    for j, prods in zigzag_plan(rank, ranks, causal):
+        c = {(a, b): case for a, b, case in prods}
+        if all(v == F for v in c.values()):
+            launches = [(0, 2, 0, 2, F)]
+        elif c == {(0, 0): D, (0, 1): S, (1, 0): F, (1, 1): D}:
+            launches = [(0, 2, 0, 2, D)]
+        elif c[0, 0] == c[0, 1] == S and c[1, 0] == c[1, 1] == F:
+            launches = [(1, 1, 0, 2, F)]
+        elif c[0, 1] == c[1, 1] == S and c[0, 0] == c[1, 0] == F:
+            launches = [(0, 2, 0, 1, F)]
+        else:
+            launches = [(a, 1, b, 1, case) for a, b, case in prods if case != S]
+        out.append((j, launches))
+    return out
+
+
+def launch_pairs(launch, sub_rows: int) -> int:
+    """(query, key) pairs one zigzag_launches launch folds per (batch, head)
+    entry, for sub-blocks of sub_rows rows."""
+    q_lo, q_n, kv_lo, kv_n, case = launch[:5]
+    if case == _lib.RA_CASE_DIAG:
+        r = q_n * sub_rows
+        return r * (r + 1) // 2
+    if case == _lib.RA_CASE_FULL:
+        return q_n * kv_n * sub_rows * sub_rows
+    return 0
+
+
+def _split_rows(launch) -> list:
+    """A launch of both query sub-blocks as launches of one each (the pairs of
+    the joined launch, each row sub-block's FULL pairs joined again)."""
+    q_lo, q_n, kv_lo, kv_n, case = launch
+    if q_n == 1:
+        return [launch]
+    if case == _lib.RA_CASE_FULL:
+        return [(0, 1, kv_lo, kv_n, case), (1, 1, kv_lo, kv_n, case)]
+    # the joined diagonal: (0, 0) diagonal, (1, 0) full, (1, 1) diagonal
+    return [(0, 1, 0, 1, case), (1, 1, 0, 1, _lib.RA_CASE_FULL), (1, 1, 1, 1, case)]
+
+
+def zigzag_fused_launches(rank: int, ranks: int, causal: bool) -> list:
+    """zigzag_launches with each query sub-block's first and last launch
+    marked: per step (j, [(q_lo, q_n, kv_lo, kv_n, case, fresh, final)]).  A
+    launch of both sub-blocks that is the first (last) for one of them only
+    is split per sub-block, so that RA_STEP_FRESH (RA_STEP_FINALIZE) applies
+    to exactly the rows it should."""
+    steps = [(j, list(ls)) for j, ls in zigzag_launches(rank, ranks, causal)]
+
+    def where(pick_last):
+        found = {}
+        order = [(s, n) for s, (_, ls) in enumerate(steps) for n in range(len(ls))]
+        for s, n in (reversed(order) if pick_last else order):
+            q_lo, q_n = steps[s][1][n][:2]
+            for p in range(q_lo, q_lo + q_n):
+                found.setdefault(p, (s, n))
+        return found
+
+    while True:
+        first, last = where(False), where(True)
+        split = False
+        for s, (_, ls) in enumerate(steps):
+            for n in reversed(range(len(ls))):
+                q_lo, q_n = ls[n][:2]
+                for found in (first, last):
+                    marks = [found.get(p) == (s, n) for p in range(q_lo, q_lo + q_n)]
+                    if any(marks) and not all(marks):
+                        ls[n:n + 1] = _split_rows(ls[n])
+                        split = True
+                        break
+        if not split:
+            break
+    out = []
+    for s, (j, ls) in enumerate(steps):
+        out.append((j, [(*l, first.get(l[0]) == (s, n), last.get(l[0]) == (s, n))
+                        for n, l in enumerate(ls)]))
+    return out
+
+
 class ZigzagRing:
     """One rank's ring under the zigzag partition.
 
@@ -456,6 +554,61 @@ class ZigzagRing:
                     _lib.finalize(st, stream=self.compute, o_out=finalize_outs[a][0],
                                   lse_out=finalize_outs[a][1])
         return plan
+
+    def run_block(self, st: _lib.State, q: torch.Tensor, kv_source: Callable[[int], tuple],
+                  rank: int, ranks: int, causal: bool, scale: float, init: bool = True,
+                  step_timers: list | None = None, timer_events=None, finalize_out=None) -> list:
+        """The forward ring on whole blocks: q [batch, heads, 2*sub_rows,
+        head_dim] holds the rank's sub-blocks zigzag_blocks(rank, ranks) in
+        position order within each (batch, head) entry, st is its state
+        (2*sub_rows rows), kv_source(j) returns (K_j, V_j) of rank j in the
+        same layout.  Each visit is the launches of zigzag_launches, row ranges
+        of these blocks (ra_step_strided): one per visit under the causal mask
+        where run() needs two to four.  finalize_out = (o_out, lse_out) of the
+        whole block, if given, fuses the state's init and finalize into each
+        sub-block's first and last launch.  Returns the launches per step."""
+        emu = self._block_emulator(tuple(q.shape), q.dtype, q.device)
+        if q.shape[2] % 2:
+            raise ValueError(f"a block of two equal sub-blocks has an even row count, got {q.shape[2]}")
+        half = q.shape[2] // 2
+        plan = zigzag_fused_launches(rank, ranks, causal)
+        # Fusing needs a first and a last launch for each sub-block.
+        fuse = finalize_out is not None and all(
+            any(l[0] <= p < l[0] + l[1] for _, ls in plan for l in ls) for p in range(2))
+        if init and not fuse:
+            _lib.state_init(st, emu.compute)
+
+        def rows(t, lo, n):
+            return t[:, :, lo * half:(lo + n) * half]
+
+        def fold(s, j, kv):
+            for q_lo, q_n, kv_lo, kv_n, case, first, last in plan[s][1]:
+                flags = 0
+                if fuse and init and first:
+                    flags |= _lib.RA_STEP_FRESH
+                if fuse and last:
+                    flags |= _lib.RA_STEP_FINALIZE
+                out = ((rows(finalize_out[0], q_lo, q_n), rows(finalize_out[1], q_lo, q_n))
+                       if flags & _lib.RA_STEP_FINALIZE else (None, None))
+                diag = case == _lib.RA_CASE_DIAG
+                emu.step(st.row_slice(q_lo * half, q_n * half), rows(q, q_lo, q_n),
+                         rows(kv[0], kv_lo, kv_n), rows(kv[1], kv_lo, kv_n), 0, 0, 1, diag, scale,
+                         case, step_timers, timer_events, flags, out, strided=True)
+
+        emu.visit([j for j, _ in plan], kv_source, fold, busy=lambda s: bool(plan[s][1]))
+        if finalize_out is not None and not fuse:
+            _lib.finalize(st, stream=emu.compute, o_out=finalize_out[0], lse_out=finalize_out[1])
+        return plan
+
+    def _block_emulator(self, shape, dtype, device) -> RingEmulator:
+        """The two-tensor (K, V of whole blocks) emulator of run_block, on the
+        same streams as the sub-block one, built on first use."""
+        em = getattr(self, "_blk", None)
+        if em is None or em.shape != shape or em.dtype != dtype:
+            em = RingEmulator(shape, dtype, device, self.emu.compute, self.emu.copy,
+                              staging=self.emu.staging)
+            self._blk = em
+        return em
 
     def run_backward(self, qs: Sequence[torch.Tensor], douts: Sequence[torch.Tensor],
                      lses: Sequence[torch.Tensor], deltas: Sequence[torch.Tensor],

@@ -218,7 +218,7 @@ def test_step_ex_rejects_before_enqueue(L):
     assert ex(_lib.RA_STEP_Q_BROADCAST | _lib.RA_STEP_FRESH, q=0) == _lib.RA_ERR_INVALID_ARG
     assert ex(_lib.RA_STEP_FINALIZE, ot=3) == _lib.RA_ERR_INVALID_ARG
     assert ex(_lib.RA_STEP_FINALIZE, o=A(6) + 8) == _lib.RA_ERR_INVALID_ARG
-    assert ex(_lib.RA_STEP_FINALIZE, lse=A(7) + 4) == _lib.RA_ERR_INVALID_ARG
+    assert ex(_lib.RA_STEP_FINALIZE, lse=A(7) + 2) == _lib.RA_ERR_INVALID_ARG   # lse_out: 4-byte aligned
     assert ex(_lib.RA_STEP_FRESH, q=0) == _lib.RA_ERR_INVALID_ARG
     assert ex(3, i=2) == _lib.RA_ERR_INVALID_ARG
     # flags 0 on a skipped block: nothing enqueued, as ra_step
@@ -374,3 +374,36 @@ def test_step_staged_rejects_before_enqueue(L):
     assert b"o_out" in L.ra_last_error()
     # the step's own checks still apply
     assert _staged(L, st, [ok_copy], q=A(3) + 8) == bad
+
+
+def _strided(L, st, rs, kvs, q=A(3), k=A(4), v=A(5), kv_rows=None, i=1, j=0, P=2, causal=1,
+             flags=0, o_out=None, lse_out=None):
+    kv = st.rows if kv_rows is None else kv_rows
+    return L.ra_step_strided(ctypes.byref(st), rs, q, k, v, _lib.RA_BF16, kv, kvs, i, j, P, causal,
+                             0.125, flags, o_out, _lib.RA_F32, lse_out, None, 0, None, None, None)
+
+
+def test_strided_step_rejects_before_enqueue(L):
+    st = _state(rows=128)
+    assert _strided(L, st, 127, 128) == _lib.RA_ERR_INVALID_ARG      # row stride below rows
+    assert b"row_stride" in L.ra_last_error()
+    assert _strided(L, st, 256, 100, kv_rows=128, causal=0) == _lib.RA_ERR_INVALID_ARG
+    assert b"kv_row_stride" in L.ra_last_error()
+    assert _strided(L, st, -1, 128) == _lib.RA_ERR_INVALID_ARG
+    assert _strided(L, st, 128, -5) == _lib.RA_ERR_INVALID_ARG
+    # extents that overlap: m of two heads 2^30 rows apart (2^32 bytes) reaches l
+    far = _state(rows=128, m=A(0), l=A(0) + (1 << 31), o=A(2), heads=2)
+    assert _strided(L, far, 1 << 30, 128) == _lib.RA_ERR_INVALID_ARG
+    assert b"state m and state l overlap" in L.ra_last_error()
+    # a strided state that folds nothing cannot take FRESH / FINALIZE (the state kernels are packed)
+    assert _strided(L, st, 256, 128, i=0, j=1, flags=_lib.RA_STEP_FRESH) == _lib.RA_ERR_UNSUPPORTED
+    assert _strided(L, st, 256, 128, kv_rows=0, causal=0,
+                    flags=_lib.RA_STEP_FINALIZE) == _lib.RA_ERR_UNSUPPORTED
+    # the same calls at the packed stride are the ordinary skip / empty no-ops ... minus the
+    # state kernels, which would launch: only plain no-op calls here
+    assert _strided(L, st, 128, 128, i=0, j=1) == _lib.RA_OK
+    assert _strided(L, st, 256, 128, i=0, j=1) == _lib.RA_OK
+    assert _strided(L, _state(rows=0, m=0, l=0, o=0), 0, 0, q=0, k=0, v=0) == _lib.RA_OK
+    # the checks of ra_step_staged still apply
+    assert _strided(L, _state(d=96), 128, 128) == _lib.RA_ERR_UNSUPPORTED
+    assert _strided(L, st, 256, 256, q=A(3) + 4) == _lib.RA_ERR_INVALID_ARG

@@ -104,3 +104,52 @@ def test_stage_block_needs_device_memory():
         _lib.stage_block(torch.empty(16), torch.empty(16))
     with pytest.raises(ValueError, match="contiguous"):
         _lib.stage_block(torch.empty(4, 4).t(), torch.empty(16))
+
+
+def test_row_stride_of_views():
+    """_row_stride: packed tensors and row ranges of longer blocks are
+    accepted with their entry spacing; other layouts are refused."""
+    from ring_attention_block_amd._lib import _row_stride
+    f32 = (torch.float32,)
+    big = torch.empty(2, 3, 10, 4)
+    assert _row_stride("t", big, (2, 3, 10, 4), f32) == 10
+    assert _row_stride("t", big[:, :, 4:7], (2, 3, 3, 4), f32) == 10
+    assert _row_stride("t", big[:1, :1, 4:7], (1, 1, 3, 4), f32) == 3     # one entry: its rows
+    assert _row_stride("t", big[:, :1, 2:5], (2, 1, 3, 4), f32) == 30    # one head: batch spacing
+    m = torch.empty(2, 3, 10)
+    assert _row_stride("m", m[:, :, 5:], (2, 3, 5), f32) == 10
+    with pytest.raises(ValueError):
+        _row_stride("t", big[:, :, :, :2], (2, 3, 10, 2), f32)           # rows not packed
+    with pytest.raises(ValueError):
+        _row_stride("t", big[:, ::2], (2, 2, 10, 4), f32)                # heads 20 rows apart, batch 30
+    with pytest.raises(ValueError):
+        _row_stride("t", big.transpose(2, 3), (2, 3, 4, 10), f32)
+    with pytest.raises(ValueError):
+        _row_stride("t", big, (2, 3, 10, 4), (torch.bfloat16,))
+
+
+def test_state_row_slice_shares_memory_and_stride():
+    from ring_attention_block_amd._lib import _row_stride
+    st = _lib.State(2, 3, 8, 64, device="cpu")
+    view = st.row_slice(4, 4)
+    assert view.shape == (2, 3, 4, 64)
+    assert view.c.m == st.m.data_ptr() + 4 * 4 and view.c.o == st.o.data_ptr() + 4 * 64 * 4
+    assert _row_stride("m", view.m, (2, 3, 4), (torch.float32,)) == 8
+    assert _row_stride("o", view.o, (2, 3, 4, 64), (torch.float32,)) == 8
+    with pytest.raises(ValueError):
+        st.row_slice(6, 4)
+
+
+def test_step_strided_refuses_mismatched_layouts_before_any_call():
+    st = _lib.State(1, 2, 64, 128, device="cpu").row_slice(0, 32)
+    q = torch.empty(1, 2, 64, 128, dtype=torch.bfloat16)
+    k = torch.empty(1, 2, 64, 128, dtype=torch.bfloat16)
+    # q packed at 32 rows while the state is spaced 64 apart
+    with pytest.raises(ValueError):
+        _lib.check_step_strided(st, q[:, :, :32].contiguous(), k, k)
+    # k and v spaced differently
+    with pytest.raises(ValueError):
+        _lib.check_step_strided(st, q[:, :, :32], k[:, :, :16], k[:, :, :16].contiguous())
+    # CPU tensors never reach the library
+    with pytest.raises(ValueError, match="GPU"):
+        _lib.check_step_strided(st, q[:, :, :32], k, k)

@@ -201,14 +201,15 @@ def test_zigzag_fused_init_finalize_is_bit_identical(heads, d, rows, P, dtype, c
 def test_bench_zigzag_path_every_row(rank):
     """The zigzag ring bench.py times (--partition zigzag) at the headline
     shape (32 heads, d = 128, 4096 tokens per rank in two pieces of 2048, 8
-    ranks): its own compute stream, the staging mode staging_for picks (the
-    next visit's copies carried by the piece products), init and finalize
-    fused into the first and last launched product, timing events on every
-    launch.  Both pieces, every row and head, against the oracle."""
+    ranks): each rank's two pieces in one block in position order, every
+    visit one launch on row ranges of the blocks (ZigzagRing.run_block, split
+    per piece where the fused init or finalize needs it), its own compute
+    stream, the staging mode bench.py picks, timing events on every launch.
+    Both pieces, every row and head, against the oracle."""
     import concurrent.futures as cf
     import contextlib
     from ring_attention_block_amd.hip_events import Event
-    from ring_attention_block_amd.ring import staging_for, zigzag_plan
+    from ring_attention_block_amd.ring import launch_pairs, staging_for, zigzag_fused_launches
     wl = synth.WORKLOADS["causal_bf16_h32_d128_c4096_p8"]
     sub = synth.zigzag_workload(wl)
     P = wl.blocks
@@ -216,27 +217,26 @@ def test_bench_zigzag_path_every_row(rank):
     cache = gen_blocks(sub, [(synth.ROLE_Q, b) for b in mine] +
                        [(r, b) for b in range(2 * P) for r in (synth.ROLE_K, synth.ROLE_V)])
     dev = {key: to_device(x, sub) for key, x in cache.items()}
-    qs = [dev[(synth.ROLE_Q, b)] for b in mine]
-
-    def source(j):
-        a, b = zigzag_blocks(j, P)
-        return (dev[(synth.ROLE_K, a)], dev[(synth.ROLE_K, b)],
-                dev[(synth.ROLE_V, a)], dev[(synth.ROLE_V, b)])
-
-    plan = zigzag_plan(rank, P, True)
-    skipped_visits = sum(all(c == _lib.RA_CASE_SKIP for _, _, c in prods) for _, prods in plan)
-    staging = staging_for(wl.heads, sub.rows, sub.rows, wl.head_dim, skipped_visits)
+    q = torch.cat([dev[(synth.ROLE_Q, b)] for b in mine], dim=2)
+    kv = {j: tuple(torch.cat([dev[(role, b)] for b in zigzag_blocks(j, P)], dim=2)
+                   for role in (synth.ROLE_K, synth.ROLE_V)) for j in range(P)}
+    plan = zigzag_fused_launches(rank, P, True)
+    lightest = min(sum(launch_pairs(l, sub.rows) for l in ls) for _, ls in plan)
+    staging = staging_for(wl.heads, lightest, 1, wl.head_dim, 0)
     compute = torch.cuda.Stream()
-    states = [_lib.State(1, wl.heads, sub.rows, wl.head_dim) for _ in range(2)]
-    outs = [(torch.empty((1, wl.heads, sub.rows, wl.head_dim), dtype=torch.float32, device="cuda"),
-             torch.empty((1, wl.heads, sub.rows), dtype=torch.float32, device="cuda")) for _ in range(2)]
-    launched = sum(c != _lib.RA_CASE_SKIP for _, prods in plan for _, _, c in prods)
+    st = _lib.State(1, wl.heads, 2 * sub.rows, wl.head_dim)
+    out = (torch.full((1, wl.heads, 2 * sub.rows, wl.head_dim), float("nan"), device="cuda"),
+           torch.full((1, wl.heads, 2 * sub.rows), float("nan"), device="cuda"))
+    launched = sum(len(ls) for _, ls in plan)
     timers = []
     pool = iter([Event(timing=True) for _ in range(2 * launched)])
-    ring = ZigzagRing(qs[0].shape, qs[0].dtype, "cuda", compute_stream=compute, staging=staging)
+    ring = ZigzagRing((1, wl.heads, sub.rows, wl.head_dim), q.dtype, "cuda", compute_stream=compute,
+                      staging=staging)
     _say(f"{sub.name} rank {rank}: staging {staging}, {launched} launches")
-    ring.run(states, qs, source, rank, P, True, sub.scale, step_timers=timers, timer_events=pool,
-             finalize_outs=outs)
+    ring.run_block(st, q, lambda j: kv[j], rank, P, True, sub.scale, step_timers=timers,
+                   timer_events=pool, finalize_out=out)
+    h = sub.rows
+    outs = [(out[0][:, :, n * h:(n + 1) * h], out[1][:, :, n * h:(n + 1) * h]) for n in range(2)]
     torch.cuda.synchronize()
     assert len(timers) == launched
 

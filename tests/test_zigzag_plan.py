@@ -57,3 +57,62 @@ def test_non_causal_is_all_full(P):
     for rank in range(P):
         for _, prods in zigzag_plan(rank, P, False):
             assert [c for _, _, c in prods] == [FULL] * 4
+
+
+def _covered(launch, h):
+    """(row, key) local index pairs a launch folds, for sub-blocks of h rows:
+    FULL every pair of its ranges, DIAG the lower triangle of its ranges."""
+    from ring_attention_block_amd import _lib as L_
+    q_lo, q_n, kv_lo, kv_n, case = launch[:5]
+    rows = range(q_lo * h, (q_lo + q_n) * h)
+    keys = range(kv_lo * h, (kv_lo + kv_n) * h)
+    if case == L_.RA_CASE_FULL:
+        return {(r, k) for r in rows for k in keys}
+    assert (q_lo, q_n) == (kv_lo, kv_n)
+    return {(r, k) for r in rows for k in keys if k - kv_lo * h <= r - q_lo * h}
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_launches_fold_exactly_the_allowed_positions(P, causal):
+    """zigzag_launches, with and without the fused-init/finalize splits, fold
+    each (query, key) pair of the rank's block against every visiting block
+    exactly once iff the causal mask on global positions allows it (brute
+    force over positions: sub-block b holds positions [b*h, (b+1)*h))."""
+    from ring_attention_block_amd.ring import zigzag_fused_launches, zigzag_launches
+    h = 3
+    for rank in range(P):
+        mine = zigzag_blocks(rank, P)
+        pos_q = [b * h + r for b in mine for r in range(h)]
+        for plan in (zigzag_launches(rank, P, causal), zigzag_fused_launches(rank, P, causal)):
+            assert [j for j, _ in plan] == ring_order(rank, P)
+            for j, launches in plan:
+                pos_k = [b * h + r for b in zigzag_blocks(j, P) for r in range(h)]
+                want = {(r, k) for r in range(2 * h) for k in range(2 * h)
+                        if not causal or pos_k[k] <= pos_q[r]}
+                got = []
+                for l in launches:
+                    got.extend(_covered(l, h))
+                assert len(got) == len(set(got)), (rank, j, "a pair folded twice")
+                assert set(got) == want, (rank, j)
+
+
+@pytest.mark.parametrize("P", [2, 3, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fused_launches_mark_each_sub_block_once(P, causal):
+    """Each query sub-block has exactly one launch that starts it (fresh) and
+    one that ends it (final); a marked launch covers no sub-block for which
+    it is not the first (last) launch; under the causal mask every visit but
+    those holding a split is one launch."""
+    from ring_attention_block_amd.ring import zigzag_fused_launches
+    for rank in range(P):
+        plan = zigzag_fused_launches(rank, P, causal)
+        flat = [l for _, ls in plan for l in ls]
+        for p in range(2):
+            mine = [n for n, l in enumerate(flat) if l[0] <= p < l[0] + l[1]]
+            fresh = [n for n in mine if flat[n][5]]
+            final = [n for n in mine if flat[n][6]]
+            assert fresh == [mine[0]] and final == [mine[-1]], (rank, p)
+        assert sum(len(ls) > 1 for _, ls in plan) <= 2, rank
+        if causal and rank == P - 1:
+            assert all(len(ls) == 1 for _, ls in plan)
