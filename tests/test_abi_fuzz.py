@@ -160,3 +160,51 @@ def test_broken_bwd_step_is_rejected_on_the_host(L, c):
                        c["j"], c["P"], c["causal"], c["scale"], None)
     assert rc in (_lib.RA_ERR_INVALID_ARG, _lib.RA_ERR_UNSUPPORTED), (rc, c)
     assert L.ra_last_error(), c
+
+
+STRIDE_BREAKERS = ["row_stride", "kv_row_stride", "neg_stride", "fresh_on_skip", "misalign_q",
+                   "head_dim", "scale", "extent_overlap"]
+
+
+@st.composite
+def broken_strided(draw):
+    c = dict(batch=draw(st.integers(1, 3)), heads=draw(st.integers(1, 4)),
+             rows=draw(st.integers(1, 300)), d=draw(st.sampled_from([64, 128])),
+             scale=draw(st.floats(1e-3, 2.0)), flags=0, causal=0, i=0, j=0, P=1,
+             m=A(0), l=A(1), o=A(2), q=A(3), k=A(4), v=A(5))
+    c["kv_rows"] = draw(st.integers(1, 300))
+    c["rs"] = c["rows"] + draw(st.integers(0, 300))
+    c["kvs"] = c["kv_rows"] + draw(st.integers(0, 300))
+    for b in draw(st.lists(st.sampled_from(STRIDE_BREAKERS), min_size=1, max_size=3, unique=True)):
+        if b == "row_stride":
+            c["rs"] = c["rows"] - draw(st.integers(1, c["rows"]))
+        elif b == "kv_row_stride":
+            c["kvs"] = c["kv_rows"] - draw(st.integers(1, c["kv_rows"]))
+        elif b == "neg_stride":
+            c[draw(st.sampled_from(["rs", "kvs"]))] = -draw(st.integers(1, 1 << 20))
+        elif b == "fresh_on_skip":
+            # a causal future block folds nothing; FRESH then needs a packed state
+            c.update(causal=1, kv_rows=c["rows"], kvs=max(c["kvs"], c["rows"]), i=0, j=1, P=2,
+                     flags=draw(st.sampled_from([1, 2, 3])))
+            c["rs"] = c["rows"] + draw(st.integers(1, 64))
+        elif b == "misalign_q":
+            c["q"] += draw(st.sampled_from([2, 4, 8]))
+        elif b == "head_dim":
+            c["d"] = draw(st.sampled_from([0, 32, 96, 256]))
+        elif b == "scale":
+            c["scale"] = draw(st.sampled_from([0.0, -1.0, math.inf, math.nan]))
+        elif b == "extent_overlap":
+            # m's extent over (batch*heads - 1) strides reaches l
+            c.update(batch=1, heads=2, rs=1 << 30, l=A(0) + (1 << 31))
+    return c
+
+
+@hypothesis.settings(max_examples=300, deadline=None, derandomize=True)
+@hypothesis.given(broken_strided())
+def test_broken_strided_step_is_rejected_on_the_host(L, c):
+    state = _lib.RaState(c["batch"], c["heads"], c["rows"], c["d"], c["m"], c["l"], c["o"])
+    rc = L.ra_step_strided(ctypes.byref(state), c["rs"], c["q"], c["k"], c["v"], _lib.RA_BF16,
+                           c["kv_rows"], c["kvs"], c["i"], c["j"], c["P"], c["causal"], c["scale"],
+                           c["flags"], None, _lib.RA_F32, None, None, 0, None, None, None)
+    assert rc in (_lib.RA_ERR_INVALID_ARG, _lib.RA_ERR_UNSUPPORTED), (rc, c)
+    assert L.ra_last_error(), c

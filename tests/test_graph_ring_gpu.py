@@ -116,3 +116,27 @@ def test_captured_zigzag_ring_replays_bit_identically(staging):
     outs = [(torch.empty(st.o.shape, device="cuda"), torch.empty(st.m.shape, device="cuda")) for st in states]
     _replays_match(lambda: zz.run(states, qs, source, rank, P, True, wl.scale, finalize_outs=outs),
                    zz.emu.copy if staging == "side" else None, compute, [t for pair in outs for t in pair])
+
+
+@pytest.mark.parametrize("staging", ["side", "fused"])
+@pytest.mark.parametrize("rank", [0, 1, 3])
+def test_captured_zigzag_block_ring_replays_bit_identically(staging, rank):
+    """ZigzagRing.run_block (whole blocks, strided launches, per-piece splits
+    for the fused init and finalize) captured and replayed: every replay and
+    the eager rings between them give the eager ring's outputs bit for bit."""
+    heads, d, rows, P = 2, 128, 256, 4
+    wl = synth.Workload("graph_zigzag_block", 92, heads, d, rows, P, "bf16", True, (rank,))
+    zw = synth.zigzag_workload(wl)
+    jobs = [(r, b) for b in range(zw.blocks) for r in (synth.ROLE_Q, synth.ROLE_K, synth.ROLE_V)]
+    host = gen_blocks(zw, jobs)
+    dev = {key: to_device(x, zw) for key, x in host.items()}
+    cat = lambda role, j: torch.cat([dev[(role, b)] for b in zigzag_blocks(j, P)], dim=2)
+    q = cat(synth.ROLE_Q, rank)
+    kv = {j: (cat(synth.ROLE_K, j), cat(synth.ROLE_V, j)) for j in range(P)}
+    compute = torch.cuda.Stream()
+    st = _lib.State(1, heads, 2 * zw.rows, d)
+    zz = ZigzagRing((1, heads, zw.rows, d), q.dtype, compute_stream=compute, staging=staging)
+    out = (torch.empty(st.o.shape, device="cuda"), torch.empty(st.m.shape, device="cuda"))
+    _say(f"zigzag block graph rank {rank} staging {staging}")
+    _replays_match(lambda: zz.run_block(st, q, lambda j: kv[j], rank, P, True, wl.scale, finalize_out=out),
+                   zz.emu.copy if staging == "side" else None, compute, list(out))
