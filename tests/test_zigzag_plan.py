@@ -116,3 +116,23 @@ def test_fused_launches_mark_each_sub_block_once(P, causal):
         assert sum(len(ls) > 1 for _, ls in plan) <= 2, rank
         if causal and rank == P - 1:
             assert all(len(ls) == 1 for _, ls in plan)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+@pytest.mark.parametrize("causal", [True, False])
+def test_launch_pairs_counts_what_each_launch_folds(P, causal):
+    """launch_pairs (bench.py's FLOP count of a zigzag launch) equals the
+    number of (query, key) pairs the launch folds, and over a ring the
+    rank's 1/P share of the sequence's allowed pairs."""
+    from ring_attention_block_amd.ring import launch_pairs, zigzag_fused_launches, zigzag_launches
+    h = 5
+    n = 2 * P * h
+    total = n * (n + 1) // 2 if causal else n * n
+    for rank in range(P):
+        for plan in (zigzag_launches(rank, P, causal), zigzag_fused_launches(rank, P, causal)):
+            got = 0
+            for _, launches in plan:
+                for l in launches:
+                    assert launch_pairs(l, h) == len(_covered(l, h)), l
+                    got += launch_pairs(l, h)
+            assert got * P == total, (rank, got)
