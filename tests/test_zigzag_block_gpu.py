@@ -161,3 +161,40 @@ def test_zigzag_block_every_rank(heads, d, rows, P, dtype, causal, fused, stagin
             eo = assert_close(o[0, :, n * h:(n + 1) * h].cpu().numpy(), want_o, to, what + " O")
             el = assert_close(lse[0, :, n * h:(n + 1) * h].cpu().numpy(), want_lse, tl, what + " LSE")
             _say(f"  {what}: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rank", [63, 0])
+def test_zigzag_block_million_tokens_sampled_rows(rank):
+    """The million-token sequence (8 heads, d = 128, 64 ranks x 16384 tokens)
+    under the zigzag partition as bench.py runs it (whole blocks, one strided
+    launch per visit, fused init and finalize, side staging): ranks 63 and 0,
+    64 sampled rows of each piece and every head against the oracle over all
+    keys before them."""
+    wl = synth.WORKLOADS["million_bf16_h8_d128_c16384_p64"]
+    sub = synth.zigzag_workload(wl)
+    P = wl.blocks
+    mine = zigzag_blocks(rank, P)
+    _say(f"{sub.name} rank {rank}: generating {2 * P} pieces")
+    cache = gen_blocks(sub, [(synth.ROLE_Q, b) for b in mine] +
+                       [(r, b) for b in range(2 * P) for r in (synth.ROLE_K, synth.ROLE_V)])
+    dev = {key: to_device(x, sub) for key, x in cache.items()}
+    o, lse = run_block_ring(sub, rank, P, True, dev, True, "side")
+    del dev
+    to, tl = tol_for(sub)
+    rows = synth.sample_rows(wl.seed, sub.rows, 64)
+    h = sub.rows
+    for n, piece in enumerate(mine):
+        keys = range(piece + 1)   # causal: every piece up to this one
+        parts = []
+        for hh in range(sub.heads):
+            parts.append(oracle_rank(sub, piece, keys, True, row_sel=rows, head_sel=[hh], cache=cache))
+            _say(f"  piece {piece}: oracle head {hh} over {len(keys)} pieces")
+        want_o = np.concatenate([p_[0] for p_ in parts])
+        want_lse = np.concatenate([p_[1] for p_ in parts])
+        got_o = o[0, :, n * h:(n + 1) * h].cpu().numpy()[:, rows]
+        got_l = lse[0, :, n * h:(n + 1) * h].cpu().numpy()[:, rows]
+        what = f"{sub.name} rank {rank} piece {piece}, {len(rows)} rows"
+        eo = assert_close(got_o, want_o, to, what + " O")
+        el = assert_close(got_l, want_lse, tl, what + " LSE")
+        _say(f"  {what}: max|dO|={eo:.2e} max|dLSE|={el:.2e}")
